@@ -1,0 +1,242 @@
+#!/usr/bin/env python3
+"""Throughput of one Beam MoE block on one MI355X.
+
+A step is one call of the whole hot path (router -> group-limited top-k ->
+permutation -> gate/up GEMM + SwiGLU -> down GEMM -> combine) over one batch
+of synthetic tokens, with inputs and weights already resident in HBM.
+
+Default workload: the Beam-shape decode batch (T=64, hidden 5120,
+intermediate 2560, 256 experts, 8 groups / keep 4 / top-8, x2.5), where
+reading the chosen experts' weights dominates.  --workload prefill|skewed|
+stack|tiny measures the other shapes.
+
+Prints one JSON line.  `roofline` describes the dominant kernel (gate/up):
+its average launch time comes from HIP events the library records around it
+on the launch stream during the timed loop; `achieved` is its algorithmic
+bytes (decode: bound "hbm") or FLOPs (prefill sizes: bound "mfma") per launch
+divided by that time.  `traffic` is the measured HBM traffic per launch from
+the committed rocprofv3 counter summary, when that summary was taken on the
+current kernel source.  `cpu_baseline` times the CPU oracle on a bounded
+sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+METRIC = "MoE-layer tokens/s at H=5120,E=256,k=8; % of peak MFMA / HBM GB/s"
+GEMM_SRC = os.path.join(ROOT, "sparse_moe_transformer_group_amd", "csrc", "gemm.hip")
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=None)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--workload", default="decode",
+                   choices=["decode", "prefill", "skewed", "stack", "tiny"])
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-sample-tokens", type=int, default=None)
+    p.add_argument("--copy-probe", action="store_true",
+                   help="also run one 1 GiB device copy (HBM counter calibration)")
+    return p.parse_args()
+
+
+def kernel_hash():
+    with open(GEMM_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic(workload):
+    """HBM bytes per launch of the gate/up kernel from the committed counter
+    summary, if it was taken on this kernel source."""
+    path = os.path.join(ROOT, "profiles", f"traffic_gateup_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        d = json.load(f)
+    if d.get("gemm_source_sha256_16") != kernel_hash():
+        return None
+    return d.get("bytes_per_launch")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the expert-parallel multi-GPU path is not built)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import moe_inputs as MI
+    import sparse_moe_transformer_group_amd as bm
+
+    dev = torch.device("cuda:0")
+    shape = MI.WORKLOADS[args.workload]
+    steps = args.steps if args.steps is not None else (
+        {"decode": 100, "tiny": 200}.get(args.workload, 20))
+    T, H, I, E, k = shape.T, shape.H, shape.I, shape.E, shape.k
+    layers = shape.layers
+
+    # ---- inputs resident in HBM
+    wr, wg, wu, wd = [], [], [], []
+    for l in range(layers):
+        wr.append(MI.make_router(E, H, layer=l).to(dev))
+        g, u, d = MI.make_expert_weights(E, H, I, dev, layer=l)
+        wg.append(g), wu.append(u), wd.append(d)
+    x = MI.make_x(T, H).to(dev)
+    off = MI.load_zipf_offsets(E).to(dev) if shape.offset == "zipf" else None
+    y = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    stream0 = None
+    torch.cuda.synchronize()
+
+    if layers == 1:
+        def step():
+            bm.block(x, wr[0], wg[0], wu[0], wd[0], shape.groups, shape.topk_groups, k, shape.scale,
+                     logit_offset=off, out=y, return_routing=False)
+    else:
+        stream0 = bm.stream_init(x)
+        work = stream0.clone()
+
+        def step():
+            work.copy_(stream0)
+            for l in range(layers):
+                bm.sublayer(work, l + 2, wr[l], wg[l], wu[l], wd[l], shape.groups,
+                            shape.topk_groups, k, shape.scale, keep_io=False)
+
+    # routing statistics (active experts) from one untimed call
+    if layers == 1:
+        _, _, _, counts = bm.block(x, wr[0], wg[0], wu[0], wd[0], shape.groups, shape.topk_groups, k,
+                                   shape.scale, logit_offset=off)
+        active = [int((counts > 0).sum().item())]
+    else:
+        tmp = stream0.clone()
+        active = []
+        for l in range(layers):
+            _, _, _, _, c = bm.sublayer(tmp, l + 2, wr[l], wg[l], wu[l], wd[l], shape.groups,
+                                        shape.topk_groups, k, shape.scale)
+            active.append(int((c > 0).sum().item()))
+        del tmp
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # ---- timed region
+    with bm.StageTimer(steps * layers) as timer:
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            step()
+        torch.cuda.synchronize()
+        elapsed = time.perf_counter() - t0
+    ms_step = elapsed * 1e3 / steps
+    launches = timer.calls
+    stage_ms = {n: v / max(launches, 1) for n, v in timer.result.items()}
+
+    # ---- algorithmic work (per step)
+    flops_step = layers * T * (2 * H * E + k * 6 * H * I)
+    bytes_step = sum(2 * (a * 3 * H * I) + 2 * E * H + 2 * T * H + 2 * T * H + 8 * T * k for a in active)
+    tokens_per_s = T * steps / elapsed
+    tflops = flops_step / (ms_step * 1e-3) / 1e12
+    gbs = bytes_step / (ms_step * 1e-3) / 1e9
+
+    # ---- dominant kernel: gate/up GEMM + SwiGLU
+    gu_ms = stage_ms["gateup"]
+    a_mean = sum(active) / len(active)
+    gu_bytes = a_mean * 2 * I * H * 2 + T * H * 2 + T * k * I * 2
+    gu_flops = T * k * 4 * H * I
+    hbm_bound = (gu_flops / gu_bytes) < (PEAK_BF16_TFLOPS / PEAK_HBM_GBS * 1e3)
+    if hbm_bound:
+        ach = gu_bytes / (gu_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(ach / PEAK_HBM_GBS, 4)}
+    else:
+        ach = gu_flops / (gu_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4)}
+    roof["traffic"] = measured_traffic(args.workload)
+    roof["kernel"] = "grouped_stream_kernel<2,1,*> (gate/up)" if T * k <= 32 * E else \
+        "grouped_tiled_kernel<2,...> (gate/up)"
+    roof["algorithmic_per_launch"] = {"bytes": int(gu_bytes), "flops": int(gu_flops)}
+    roof["avg_launch_ms"] = round(gu_ms, 5)
+
+    if args.copy_probe:
+        a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
+
+    out = {
+        "metric": METRIC,
+        "value": round(tokens_per_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"beam_moe_{args.workload}", "T": T, "H": H, "I": I, "E": E,
+                   "groups": shape.groups, "topk_groups": shape.topk_groups, "k": k,
+                   "scale": shape.scale, "layers": layers,
+                   "logit_offset": shape.offset, "active_experts": active},
+        "tflops": round(tflops, 1),
+        "frac_peak_mfma": round(tflops / PEAK_BF16_TFLOPS, 4),
+        "algorithmic_gbs": round(gbs, 1),
+        "frac_peak_hbm": round(gbs / PEAK_HBM_GBS, 4),
+        "stage_ms": {n: round(v, 5) for n, v in stage_ms.items()},
+        "roofline": roof,
+    }
+
+    # ---- CPU oracle baseline on a bounded sample
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(args, shape, x, wr[0], wg[0], wu[0], wd[0], off)
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(args, shape, x, wr, wg, wu, wd, off):
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    import oracle as O
+    from moe_inputs import bf16_bits
+
+    n = args.cpu_sample_tokens or {"decode": 4, "tiny": 128}.get(args.workload, 4)
+    n = min(n, shape.T)
+    xb = bf16_bits(x[:n])
+    wrb = bf16_bits(wr)
+    offn = None if off is None else off.cpu().numpy()
+    # stage the sampled tokens' expert weights in host memory (not timed)
+    z = O.router_logits(xb, wrb, offn)
+    ids, _, _, _ = O.group_limited_topk(O.sigmoid(z), shape.groups, shape.topk_groups, shape.k,
+                                        shape.scale)
+    host = {int(e): (bf16_bits(wg[e]), bf16_bits(wu[e]), bf16_bits(wd[e])) for e in np.unique(ids)}
+    t0 = time.perf_counter()
+    O.moe_block(xb, wrb, lambda e: host[e], shape.groups, shape.topk_groups, shape.k, shape.scale,
+                offn)
+    dt = time.perf_counter() - t0
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    return {"value": round(n / dt, 3), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"first {n} tokens of the {shape.name} batch (T={shape.T}), whole block in FP64 "
+                      f"({len(host)} experts' weights staged in host memory beforehand), "
+                      f"{dt:.1f} s"}
+
+
+if __name__ == "__main__":
+    main()

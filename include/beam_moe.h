@@ -1,0 +1,185 @@
+/*
+ * beam_moe.h -- C ABI of libbeam_moe.so, one Beam Mixture-of-Experts block on
+ * an AMD Instinct MI355X (gfx950).
+ *
+ * Source pages (cited by title and section):
+ *   [MoE] "Willkommen Beam: ein offenes 501B-Modell, das Sie besitzen,
+ *         anpassen und skalieren können" (spke.com), section "Mixture of
+ *         Experts"; the same paragraph on "Reflection 发布 501B 开放模型 Beam，
+ *         支持自托管定制与扩展" (sihot.dev), section 混合专家（Mixture of Experts）.
+ *   [RES] the same pages, section "Residual Stream".
+ *
+ * Conventions shared by every entry point
+ *   - Tensors are DEVICE pointers, row-major and contiguous.  "bf16" tensors
+ *     are uint16_t bit patterns.  Every pointer must be 16-byte aligned.
+ *   - The caller owns every buffer, including the workspace; the library
+ *     never allocates, frees or synchronises device memory.  Work is enqueued
+ *     on `stream` (a hipStream_t; NULL = the default stream) and is complete
+ *     when that stream is synchronised.  Inputs are never written; outputs
+ *     are overwritten in full; outputs must not alias inputs.  Workspace
+ *     contents are not preserved between calls, so two calls in flight at the
+ *     same time must use different workspaces.
+ *   - Return value: 0 on success, a negative BEAM_MOE_ERR_* code otherwise.
+ *     Every argument check runs on the host before any HIP call, so a call
+ *     that fails validation enqueues nothing.  T == 0 with valid dimensions
+ *     returns 0 and enqueues nothing; pointers and workspace size are not
+ *     examined then (empty tensors may have NULL data pointers).  HIP_ERROR reports a launch failure (hipGetLastError); a fault
+ *     inside a kernel surfaces at the caller's next synchronisation.
+ *   - Dimension rules (the Beam shapes satisfy all of them):
+ *       0 <= T <= 2^24;  H, I in [64, 32768] and multiples of 64;
+ *       1 <= E <= 512;  E % groups == 0 and E / groups >= 2;
+ *       1 <= topk_groups <= groups;  1 <= k <= min(32, topk_groups * E / groups)
+ *       (route / block); 1 <= k <= 32 (forward / permute); scale finite.
+ *   - Device data (id range, weight values) is not validated: routing ids
+ *     outside [0, E) are dropped (they contribute nothing and are not counted).
+ *   - The first compute call on a device checks that it is gfx950
+ *     (UNSUPPORTED_DEVICE otherwise).
+ *   - The library is stateless apart from a per-device property cache and the
+ *     optional stage timer; calls from several host threads are safe.
+ */
+#ifndef BEAM_MOE_H
+#define BEAM_MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define BEAM_MOE_OK 0
+#define BEAM_MOE_ERR_INVALID_DIM (-1)
+#define BEAM_MOE_ERR_NULL_POINTER (-2)
+#define BEAM_MOE_ERR_MISALIGNED (-3)
+#define BEAM_MOE_ERR_WORKSPACE_TOO_SMALL (-4)
+#define BEAM_MOE_ERR_UNSUPPORTED_DEVICE (-5)
+#define BEAM_MOE_ERR_HIP (-6)
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* beam_moe_status_string(int status);
+
+/* Library version, "major.minor.patch" (static string). */
+const char* beam_moe_version(void);
+
+/* Bytes of workspace that route, permute, forward, block and sublayer need
+ * for these sizes (the maximum over all of them).  Returns 0 if the sizes
+ * break the dimension rules. */
+size_t beam_moe_workspace_bytes(int64_t T, int H, int I, int E, int k);
+
+/*
+ * Router + group-limited top-k  ([MoE]; router in FP32 per [RES]).
+ *   z[t,e]  = sum_h x[t,h] * w_router[e,h]  (+ logit_offset[e])   FP32 accumulate
+ *   s[t,e]  = 1 / (1 + exp(-z[t,e]))                               FP32
+ *   group g = experts [g*E/groups, (g+1)*E/groups); its score is the sum of its
+ *             two largest s; the topk_groups best groups are kept;
+ *   the k largest s among experts of kept groups are selected (exact ties go
+ *   to the lower index), ordered by decreasing s;
+ *   topk_weights[t,j] = scale * (s_j / sum of the k selected s).
+ * x            [T,H] bf16          w_router [E,H] bf16
+ * logit_offset [E] fp32 or NULL (added to the logit before the sigmoid)
+ * topk_ids     [T,k] int32 out     topk_weights [T,k] fp32 out
+ * expert_counts[E] int32 out or NULL (number of tokens that picked each expert)
+ */
+int beam_moe_route(void* stream, int64_t T, int H, int E, int groups, int topk_groups, int k,
+                   float scale, const uint16_t* x, const uint16_t* w_router,
+                   const float* logit_offset, int32_t* topk_ids, float* topk_weights,
+                   int32_t* expert_counts, void* workspace, size_t workspace_bytes);
+
+/*
+ * Token permutation: the (token, slot) assignments a = t*k + j sorted by
+ * expert id with a stable sort (ascending token order inside an expert).
+ * topk_ids       [T,k] int32 in
+ * expert_counts  [E] int32 out      expert_offsets [E+1] int32 out (exclusive scan)
+ * sorted_tokens  [T*k] int32 out    token of each expert-major row; entries
+ *                                   past expert_offsets[E] are left untouched
+ * row_of         [T*k] int32 out    expert-major row of each assignment, -1 for
+ *                                   an id outside [0, E)
+ */
+int beam_moe_permute(void* stream, int64_t T, int E, int k, const int32_t* topk_ids,
+                     int32_t* expert_counts, int32_t* expert_offsets, int32_t* sorted_tokens,
+                     int32_t* row_of, void* workspace, size_t workspace_bytes);
+
+/*
+ * Experts + combine with given routing  ([MoE]; SwiGLU product in FP32 per [RES]).
+ *   for each assignment (t, j) with e = topk_ids[t,j] in [0, E):
+ *     g = w_gate[e] . x[t],  u = w_up[e] . x[t]              (FP32 accumulate)
+ *     h = bf16( g / (1 + exp(-g)) * u )                       (FP32, one rounding)
+ *     o = w_down[e] . h                                       (FP32 accumulate)
+ *   y[t] = bf16( sum_j topk_weights[t,j] * o_j )   FP32 sum in slot order j = 0..k-1
+ * topk_weights are used as given (the router's weights already hold the scale).
+ * x [T,H] bf16; w_gate, w_up [E,I,H] bf16; w_down [E,H,I] bf16; y [T,H] bf16 out;
+ * expert_counts [E] int32 out or NULL.
+ */
+int beam_moe_forward(void* stream, int64_t T, int H, int I, int E, int k, const uint16_t* x,
+                     const int32_t* topk_ids, const float* topk_weights, const uint16_t* w_gate,
+                     const uint16_t* w_up, const uint16_t* w_down, uint16_t* y,
+                     int32_t* expert_counts, void* workspace, size_t workspace_bytes);
+
+/*
+ * Whole block: route -> permute -> gate/up GEMM + SwiGLU -> down GEMM -> combine.
+ * Same arguments and meaning as route and forward.  topk_ids / topk_weights /
+ * expert_counts are outputs and may each be NULL (then they live in the
+ * workspace and are not returned).
+ */
+int beam_moe_block(void* stream, int64_t T, int H, int I, int E, int groups, int topk_groups,
+                   int k, float scale, const uint16_t* x, const uint16_t* w_router,
+                   const float* logit_offset, const uint16_t* w_gate, const uint16_t* w_up,
+                   const uint16_t* w_down, uint16_t* y, int32_t* topk_ids, float* topk_weights,
+                   int32_t* expert_counts, void* workspace, size_t workspace_bytes);
+
+/*
+ * Residual stream helpers  ([RES]: every sublayer is normalised before and
+ * after; the embedding is residual step 1; at step >= 2 the stream keeps
+ * sqrt((step-1)/step) of itself and adds 1/sqrt(step) of the sublayer output).
+ * RMSNorm here is v / sqrt(mean(v^2) + eps) with unit gain, in FP32.
+ *
+ * beam_moe_stream_init:    stream[T,H] fp32 out = x[T,H] bf16 widened.
+ * beam_moe_rmsnorm:        out[T,H] bf16 = bf16(RMSNorm(in[T,H] fp32)).
+ * beam_moe_residual_update: stream[T,H] fp32 in/out =
+ *                   sqrt((step-1)/step)*stream + RMSNorm(float(y)) / sqrt(step),
+ *                   y [T,H] bf16; step >= 2.
+ * beam_moe_sublayer: one sandwich-normed MoE sublayer at residual step `step`:
+ *                   x_in = rmsnorm(stream); y = block(x_in); residual_update(y).
+ *                   moe_input / moe_output [T,H] bf16 receive x_in and y when
+ *                   not NULL; topk_ids / topk_weights / expert_counts as in block.
+ */
+int beam_moe_stream_init(void* stream, int64_t T, int H, const uint16_t* x, float* stream_out);
+int beam_moe_rmsnorm(void* stream, int64_t T, int H, float eps, const float* in, uint16_t* out);
+int beam_moe_residual_update(void* stream, int64_t T, int H, float eps, int step,
+                             const uint16_t* y, float* stream_io);
+int beam_moe_sublayer(void* stream, int64_t T, int H, int I, int E, int groups, int topk_groups,
+                      int k, float scale, float eps, int step, float* stream_io,
+                      const uint16_t* w_router, const uint16_t* w_gate, const uint16_t* w_up,
+                      const uint16_t* w_down, uint16_t* moe_input, uint16_t* moe_output,
+                      int32_t* topk_ids, float* topk_weights, int32_t* expert_counts,
+                      void* workspace, size_t workspace_bytes);
+
+/*
+ * Expert-GEMM schedule for later calls in this process: 0 = automatic (the
+ * weight-streaming schedule when there are at most ~32 assignments per
+ * expert on average, the LDS-tiled schedule otherwise), 1 = always
+ * streaming, 2 = always tiled.  Both give the same results up to FP32
+ * summation order inside the MFMA accumulations.  Returns INVALID_DIM for
+ * another mode.
+ */
+int beam_moe_set_schedule(int mode);
+
+/*
+ * Stage timer (measurement aid).  After beam_moe_timer_begin(max_calls), each
+ * block / forward call (up to max_calls of them) records a hipEvent before
+ * and after each of its stages on its stream.  beam_moe_timer_end
+ * synchronises those events, writes the summed milliseconds of each stage
+ * into stage_ms[0 .. n_stages-1] (n_stages >= beam_moe_stage_count()), the
+ * number of timed calls into *n_calls, and releases the events.  One timer
+ * per process; not for concurrent use from several threads.
+ */
+int beam_moe_stage_count(void);
+const char* beam_moe_stage_name(int stage);
+int beam_moe_timer_begin(int max_calls);
+int beam_moe_timer_end(double* stage_ms, int n_stages, int* n_calls);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BEAM_MOE_H */

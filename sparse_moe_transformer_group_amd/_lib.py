@@ -1,0 +1,314 @@
+"""ctypes binding of libbeam_moe.so (declarations in include/beam_moe.h).
+
+Argument marshalling only: tensors are checked for device, dtype, shape and
+contiguity, and their device pointers, the sizes and torch's current HIP
+stream are passed to the C ABI.  Every step of the block runs in the HIP
+kernels of the library.  There is no fallback: if the library is missing or
+cannot be loaded, importing this module raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+import threading
+from typing import Optional
+
+import torch
+
+from .build import LIB_PATH
+
+_c_i64 = ctypes.c_int64
+_c_int = ctypes.c_int
+_c_f = ctypes.c_float
+_c_vp = ctypes.c_void_p
+_c_sz = ctypes.c_size_t
+
+STATUS = {
+    0: "ok", -1: "invalid dimension", -2: "null pointer", -3: "misaligned pointer",
+    -4: "workspace too small", -5: "unsupported device", -6: "HIP error",
+}
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is not built; run `python -c 'import __graft_entry__ as g; g.build()'` "
+            "or `python -m sparse_moe_transformer_group_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    sig = {
+        "beam_moe_status_string": (ctypes.c_char_p, [_c_int]),
+        "beam_moe_version": (ctypes.c_char_p, []),
+        "beam_moe_workspace_bytes": (_c_sz, [_c_i64, _c_int, _c_int, _c_int, _c_int]),
+        "beam_moe_route": (_c_int, [_c_vp, _c_i64, _c_int, _c_int, _c_int, _c_int, _c_int, _c_f,
+                                    _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_sz]),
+        "beam_moe_permute": (_c_int, [_c_vp, _c_i64, _c_int, _c_int, _c_vp, _c_vp, _c_vp, _c_vp,
+                                      _c_vp, _c_vp, _c_sz]),
+        "beam_moe_forward": (_c_int, [_c_vp, _c_i64, _c_int, _c_int, _c_int, _c_int, _c_vp, _c_vp,
+                                      _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_sz]),
+        "beam_moe_block": (_c_int, [_c_vp, _c_i64, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
+                                    _c_f, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp,
+                                    _c_vp, _c_vp, _c_vp, _c_sz]),
+        "beam_moe_stream_init": (_c_int, [_c_vp, _c_i64, _c_int, _c_vp, _c_vp]),
+        "beam_moe_rmsnorm": (_c_int, [_c_vp, _c_i64, _c_int, _c_f, _c_vp, _c_vp]),
+        "beam_moe_residual_update": (_c_int, [_c_vp, _c_i64, _c_int, _c_f, _c_int, _c_vp, _c_vp]),
+        "beam_moe_sublayer": (_c_int, [_c_vp, _c_i64, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
+                                       _c_f, _c_f, _c_int, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp,
+                                       _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_sz]),
+        "beam_moe_set_schedule": (_c_int, [_c_int]),
+        "beam_moe_stage_count": (_c_int, []),
+        "beam_moe_stage_name": (ctypes.c_char_p, [_c_int]),
+        "beam_moe_timer_begin": (_c_int, [_c_int]),
+        "beam_moe_timer_end": (_c_int, [ctypes.POINTER(ctypes.c_double), _c_int,
+                                        ctypes.POINTER(_c_int)]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+lib = _load()
+
+
+class BeamMoeError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        msg = lib.beam_moe_status_string(status).decode()
+        super().__init__(f"{fn} failed: {msg} ({status})")
+        self.status = status
+
+
+def _check(fn: str, status: int):
+    if status != 0:
+        if status in (-1, -2, -3, -4):
+            raise ValueError(f"{fn}: {lib.beam_moe_status_string(status).decode()} ({status})")
+        raise BeamMoeError(fn, status)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _dev_tensor(t, name, dtype, shape=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a HIP device, found {t.device}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, found {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, found {tuple(t.shape)}")
+    return t
+
+
+def _stream(device: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+_ws_lock = threading.Lock()
+_ws_cache = {}
+
+
+def workspace_bytes(T: int, H: int, I: int, E: int, k: int) -> int:
+    n = lib.beam_moe_workspace_bytes(T, H, I, E, k)
+    if n == 0 and T >= 0:
+        raise ValueError("dimensions break the library's rules")
+    return int(n)
+
+
+def get_workspace(device: torch.device, nbytes: int) -> torch.Tensor:
+    """Per-device workspace buffer, grown on demand and reused across calls."""
+    key = (device.type, device.index)
+    with _ws_lock:
+        buf = _ws_cache.get(key)
+        if buf is None or buf.numel() < nbytes:
+            buf = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+            _ws_cache[key] = buf
+        return buf
+
+
+def release_workspaces():
+    with _ws_lock:
+        _ws_cache.clear()
+
+
+def version() -> str:
+    return lib.beam_moe_version().decode()
+
+
+def set_schedule(mode: str):
+    """'auto', 'stream' or 'tiled' expert-GEMM schedule for later calls."""
+    code = {"auto": 0, "stream": 1, "tiled": 2}[mode]
+    _check("beam_moe_set_schedule", lib.beam_moe_set_schedule(code))
+
+
+def route(x, w_router, groups=8, topk_groups=4, k=8, scale=2.5, logit_offset=None,
+          return_counts=True):
+    """Router + group-limited top-k.  Returns (ids int32 [T,k], weights fp32 [T,k], counts)."""
+    T, H = x.shape
+    E = w_router.shape[0]
+    dev = x.device
+    _dev_tensor(x, "x", torch.bfloat16, (T, H))
+    _dev_tensor(w_router, "w_router", torch.bfloat16, (E, H))
+    if logit_offset is not None:
+        _dev_tensor(logit_offset, "logit_offset", torch.float32, (E,))
+    ids = torch.empty((T, k), dtype=torch.int32, device=dev)
+    w = torch.empty((T, k), dtype=torch.float32, device=dev)
+    counts = torch.empty((E,), dtype=torch.int32, device=dev) if return_counts else None
+    nbytes = workspace_bytes(T, H, 64, E, k)
+    ws = get_workspace(dev, nbytes)
+    rc = lib.beam_moe_route(_stream(dev), T, H, E, groups, topk_groups, k, float(scale), _ptr(x),
+                            _ptr(w_router), _ptr(logit_offset), _ptr(ids), _ptr(w), _ptr(counts),
+                            _ptr(ws), ws.numel())
+    _check("beam_moe_route", rc)
+    return ids, w, counts
+
+
+def permute(topk_ids, E):
+    """Expert-major order of the assignments: (counts, offsets, sorted_tokens, row_of)."""
+    T, k = topk_ids.shape
+    dev = topk_ids.device
+    _dev_tensor(topk_ids, "topk_ids", torch.int32, (T, k))
+    counts = torch.empty((E,), dtype=torch.int32, device=dev)
+    offsets = torch.empty((E + 1,), dtype=torch.int32, device=dev)
+    sorted_tokens = torch.full((max(T * k, 1),), -1, dtype=torch.int32, device=dev)[:T * k]
+    row_of = torch.empty((T * k,), dtype=torch.int32, device=dev)
+    ws = get_workspace(dev, workspace_bytes(T, 64, 64, E, k))
+    rc = lib.beam_moe_permute(_stream(dev), T, E, k, _ptr(topk_ids), _ptr(counts), _ptr(offsets),
+                              _ptr(sorted_tokens), _ptr(row_of), _ptr(ws), ws.numel())
+    _check("beam_moe_permute", rc)
+    return counts, offsets, sorted_tokens, row_of
+
+
+def _expert_shapes(w_gate, w_up, w_down):
+    E, I, H = w_gate.shape
+    _dev_tensor(w_gate, "w_gate", torch.bfloat16, (E, I, H))
+    _dev_tensor(w_up, "w_up", torch.bfloat16, (E, I, H))
+    _dev_tensor(w_down, "w_down", torch.bfloat16, (E, H, I))
+    return E, I, H
+
+
+def forward(x, topk_ids, topk_weights, w_gate, w_up, w_down, return_counts=False):
+    """Experts + combine with given routing.  Returns y bf16 [T,H] (and counts)."""
+    E, I, H = _expert_shapes(w_gate, w_up, w_down)
+    T, k = topk_ids.shape
+    dev = x.device
+    _dev_tensor(x, "x", torch.bfloat16, (T, H))
+    _dev_tensor(topk_ids, "topk_ids", torch.int32, (T, k))
+    _dev_tensor(topk_weights, "topk_weights", torch.float32, (T, k))
+    y = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    counts = torch.empty((E,), dtype=torch.int32, device=dev) if return_counts else None
+    ws = get_workspace(dev, workspace_bytes(T, H, I, E, k))
+    rc = lib.beam_moe_forward(_stream(dev), T, H, I, E, k, _ptr(x), _ptr(topk_ids),
+                              _ptr(topk_weights), _ptr(w_gate), _ptr(w_up), _ptr(w_down), _ptr(y),
+                              _ptr(counts), _ptr(ws), ws.numel())
+    _check("beam_moe_forward", rc)
+    return (y, counts) if return_counts else y
+
+
+def block(x, w_router, w_gate, w_up, w_down, groups=8, topk_groups=4, k=8, scale=2.5,
+          logit_offset=None, out=None, return_routing=True):
+    """Whole MoE block.  Returns (y, ids, weights, counts) or y."""
+    E, I, H = _expert_shapes(w_gate, w_up, w_down)
+    T = x.shape[0]
+    dev = x.device
+    _dev_tensor(x, "x", torch.bfloat16, (T, H))
+    _dev_tensor(w_router, "w_router", torch.bfloat16, (E, H))
+    if logit_offset is not None:
+        _dev_tensor(logit_offset, "logit_offset", torch.float32, (E,))
+    y = out if out is not None else torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    _dev_tensor(y, "out", torch.bfloat16, (T, H))
+    ids = w = counts = None
+    if return_routing:
+        ids = torch.empty((T, k), dtype=torch.int32, device=dev)
+        w = torch.empty((T, k), dtype=torch.float32, device=dev)
+        counts = torch.empty((E,), dtype=torch.int32, device=dev)
+    ws = get_workspace(dev, workspace_bytes(T, H, I, E, k))
+    rc = lib.beam_moe_block(_stream(dev), T, H, I, E, groups, topk_groups, k, float(scale), _ptr(x),
+                            _ptr(w_router), _ptr(logit_offset), _ptr(w_gate), _ptr(w_up),
+                            _ptr(w_down), _ptr(y), _ptr(ids), _ptr(w), _ptr(counts), _ptr(ws),
+                            ws.numel())
+    _check("beam_moe_block", rc)
+    return (y, ids, w, counts) if return_routing else y
+
+
+def stream_init(x):
+    T, H = x.shape
+    _dev_tensor(x, "x", torch.bfloat16, (T, H))
+    s = torch.empty((T, H), dtype=torch.float32, device=x.device)
+    _check("beam_moe_stream_init", lib.beam_moe_stream_init(_stream(x.device), T, H, _ptr(x), _ptr(s)))
+    return s
+
+
+def rmsnorm(v, eps=1e-6):
+    T, H = v.shape
+    _dev_tensor(v, "in", torch.float32, (T, H))
+    out = torch.empty((T, H), dtype=torch.bfloat16, device=v.device)
+    _check("beam_moe_rmsnorm", lib.beam_moe_rmsnorm(_stream(v.device), T, H, float(eps), _ptr(v), _ptr(out)))
+    return out
+
+
+def residual_update(stream_io, y, step, eps=1e-6):
+    T, H = stream_io.shape
+    _dev_tensor(stream_io, "stream", torch.float32, (T, H))
+    _dev_tensor(y, "y", torch.bfloat16, (T, H))
+    _check("beam_moe_residual_update",
+           lib.beam_moe_residual_update(_stream(y.device), T, H, float(eps), int(step), _ptr(y),
+                                        _ptr(stream_io)))
+    return stream_io
+
+
+def sublayer(stream_io, step, w_router, w_gate, w_up, w_down, groups=8, topk_groups=4, k=8,
+             scale=2.5, eps=1e-6, keep_io=True):
+    """One sandwich-normed MoE sublayer + residual update, in place on stream_io.
+    Returns (moe_input, moe_output, ids, weights, counts) when keep_io."""
+    E, I, H = _expert_shapes(w_gate, w_up, w_down)
+    T = stream_io.shape[0]
+    dev = stream_io.device
+    _dev_tensor(stream_io, "stream", torch.float32, (T, H))
+    _dev_tensor(w_router, "w_router", torch.bfloat16, (E, H))
+    xin = yb = ids = w = counts = None
+    if keep_io:
+        xin = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+        yb = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+        ids = torch.empty((T, k), dtype=torch.int32, device=dev)
+        w = torch.empty((T, k), dtype=torch.float32, device=dev)
+        counts = torch.empty((E,), dtype=torch.int32, device=dev)
+    ws = get_workspace(dev, workspace_bytes(T, H, I, E, k))
+    rc = lib.beam_moe_sublayer(_stream(dev), T, H, I, E, groups, topk_groups, k, float(scale),
+                               float(eps), int(step), _ptr(stream_io), _ptr(w_router), _ptr(w_gate),
+                               _ptr(w_up), _ptr(w_down), _ptr(xin), _ptr(yb), _ptr(ids), _ptr(w),
+                               _ptr(counts), _ptr(ws), ws.numel())
+    _check("beam_moe_sublayer", rc)
+    return (xin, yb, ids, w, counts) if keep_io else None
+
+
+def stage_names():
+    return [lib.beam_moe_stage_name(i).decode() for i in range(lib.beam_moe_stage_count())]
+
+
+class StageTimer:
+    """Per-stage hipEvent timing of the next `max_calls` block/forward calls."""
+
+    def __init__(self, max_calls: int):
+        self.max_calls = max_calls
+        self.result = None
+
+    def __enter__(self):
+        _check("beam_moe_timer_begin", lib.beam_moe_timer_begin(self.max_calls))
+        return self
+
+    def __exit__(self, *exc):
+        n = lib.beam_moe_stage_count()
+        arr = (ctypes.c_double * n)()
+        calls = _c_int(0)
+        rc = lib.beam_moe_timer_end(arr, n, ctypes.byref(calls))
+        if exc[0] is None:
+            _check("beam_moe_timer_end", rc)
+        names = stage_names()
+        self.calls = calls.value
+        self.result = {names[i]: arr[i] for i in range(n)}
+        return False

@@ -1,0 +1,477 @@
+// C ABI of libbeam_moe: argument validation, workspace layout, launch order.
+// The contract of every entry point is documented in include/beam_moe.h.
+#include <math.h>
+#include <string.h>
+
+#include <atomic>
+#include <mutex>
+#include <vector>
+
+#include "../../include/beam_moe.h"
+#include "common.h"
+#include "kernels.h"
+
+using namespace beam;
+
+namespace {
+
+constexpr int64_t kMaxT = int64_t(1) << 24;
+constexpr int kMaxE = 512;
+constexpr int kMaxK = 32;
+constexpr int kMaxDim = 32768;
+
+// ---------------------------------------------------------------- validation
+bool bad_dim64(int v) { return v < 64 || v > kMaxDim || (v % 64) != 0; }
+bool misaligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
+
+int check_route_dims(int64_t T, int H, int E, int groups, int topk_groups, int k, float scale) {
+  if (T < 0 || T > kMaxT || bad_dim64(H)) return BEAM_MOE_ERR_INVALID_DIM;
+  if (E < 1 || E > kMaxE || groups < 1 || E % groups != 0 || E / groups < 2)
+    return BEAM_MOE_ERR_INVALID_DIM;
+  if (topk_groups < 1 || topk_groups > groups) return BEAM_MOE_ERR_INVALID_DIM;
+  if (k < 1 || k > kMaxK || k > topk_groups * (E / groups)) return BEAM_MOE_ERR_INVALID_DIM;
+  if (!isfinite(scale)) return BEAM_MOE_ERR_INVALID_DIM;
+  return BEAM_MOE_OK;
+}
+
+int check_forward_dims(int64_t T, int H, int I, int E, int k) {
+  if (T < 0 || T > kMaxT || bad_dim64(H) || bad_dim64(I)) return BEAM_MOE_ERR_INVALID_DIM;
+  if (E < 1 || E > kMaxE || k < 1 || k > kMaxK) return BEAM_MOE_ERR_INVALID_DIM;
+  return BEAM_MOE_OK;
+}
+
+// nullable: pointers that may be NULL.
+int check_ptrs(std::initializer_list<const void*> required, std::initializer_list<const void*> nullable) {
+  for (const void* p : required)
+    if (!p) return BEAM_MOE_ERR_NULL_POINTER;
+  for (const void* p : required)
+    if (misaligned(p)) return BEAM_MOE_ERR_MISALIGNED;
+  for (const void* p : nullable)
+    if (p && misaligned(p)) return BEAM_MOE_ERR_MISALIGNED;
+  return BEAM_MOE_OK;
+}
+
+// ---------------------------------------------------------------- workspace
+size_t align256(size_t b) { return (b + 255) & ~size_t(255); }
+
+struct Layout {
+  size_t zpart, ids, w, counts, offsets, hist, base, sorted, rowof, h, o, xin, y, total;
+  int S;
+};
+
+// Route needs only the logit partials; permute only the histograms.
+Layout route_layout(int64_t T, int H, int E) {
+  Layout L{};
+  L.S = router_splits(T, H, E);
+  L.zpart = 0;
+  L.total = align256((size_t)L.S * T * E * 4);
+  return L;
+}
+
+Layout perm_layout(int64_t T, int E, int k) {
+  Layout L{};
+  const size_t NB = (size_t)perm_blocks(T * k);
+  L.counts = 0;
+  L.hist = align256((size_t)E * 4);
+  L.base = L.hist + align256(NB * E * 4);
+  L.total = L.base + align256(NB * E * 4);
+  return L;
+}
+
+Layout layout(int64_t T, int H, int I, int E, int k) {
+  Layout L{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t at = off;
+    off += align256(bytes);
+    return at;
+  };
+  const size_t Tk = (size_t)T * k;
+  const size_t NB = (size_t)perm_blocks((int64_t)Tk);
+  L.S = router_splits(T, H, E);
+  L.zpart = take((size_t)L.S * T * E * 4);
+  L.ids = take(Tk * 4);
+  L.w = take(Tk * 4);
+  L.counts = take((size_t)E * 4);
+  L.offsets = take((size_t)(E + 1) * 4);
+  L.hist = take(NB * E * 4);
+  L.base = take(NB * E * 4);
+  L.sorted = take(Tk * 4);
+  L.rowof = take(Tk * 4);
+  L.h = take(Tk * (size_t)I * 2);
+  L.o = take(Tk * (size_t)H * 4);
+  L.xin = take((size_t)T * H * 2);
+  L.y = take((size_t)T * H * 2);
+  L.total = off;
+  return L;
+}
+
+// ---------------------------------------------------------------- device
+struct DevInfo {
+  std::atomic<int> state{0};  // 0 unknown, 1 ok, -1 unsupported
+  int num_cu = 256;
+};
+DevInfo g_dev[64];
+std::mutex g_dev_mu;
+
+int device_check(int* num_cu) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return BEAM_MOE_ERR_HIP;
+  DevInfo& d = g_dev[dev];
+  int s = d.state.load(std::memory_order_acquire);
+  if (s == 0) {
+    std::lock_guard<std::mutex> lk(g_dev_mu);
+    s = d.state.load(std::memory_order_relaxed);
+    if (s == 0) {
+      hipDeviceProp_t p;
+      if (hipGetDeviceProperties(&p, dev) != hipSuccess) return BEAM_MOE_ERR_HIP;
+      d.num_cu = p.multiProcessorCount;
+      s = (strncmp(p.gcnArchName, "gfx950", 6) == 0) ? 1 : -1;
+      d.state.store(s, std::memory_order_release);
+    }
+  }
+  if (s < 0) return BEAM_MOE_ERR_UNSUPPORTED_DEVICE;
+  *num_cu = d.num_cu;
+  return BEAM_MOE_OK;
+}
+
+// ---------------------------------------------------------------- schedule knob
+std::atomic<int> g_schedule{0};  // 0 auto, 1 stream, 2 tiled
+
+bool use_stream(int64_t T, int k, int E) {
+  const int m = g_schedule.load(std::memory_order_relaxed);
+  if (m == 1) return true;
+  if (m == 2) return false;
+  return (double)T * k <= 32.0 * E;  // up to ~32 tokens per expert on average
+}
+
+// ---------------------------------------------------------------- stage timer
+enum Stage { ST_LOGITS, ST_SELECT, ST_PERMUTE, ST_GATEUP, ST_DOWN, ST_COMBINE, NST };
+const char* kStageNames[NST] = {"router_logits", "select", "permute", "gateup", "down", "combine"};
+
+struct Timer {
+  std::mutex mu;
+  bool on = false;
+  int max_calls = 0, n_calls = 0;
+  std::vector<hipEvent_t> ev;  // [call][stage][2]
+  std::vector<char> used;      // [call][stage]
+} g_timer;
+
+int timer_claim() {
+  std::lock_guard<std::mutex> lk(g_timer.mu);
+  if (!g_timer.on || g_timer.n_calls >= g_timer.max_calls) return -1;
+  return g_timer.n_calls++;
+}
+
+struct StageScope {
+  int slot, stage;
+  hipStream_t st;
+  StageScope(int slot_, int stage_, hipStream_t st_) : slot(slot_), stage(stage_), st(st_) {
+    if (slot >= 0) {
+      (void)hipEventRecord(g_timer.ev[(size_t)(slot * NST + stage) * 2], st);
+      g_timer.used[(size_t)slot * NST + stage] = 1;
+    }
+  }
+  ~StageScope() {
+    if (slot >= 0) (void)hipEventRecord(g_timer.ev[(size_t)(slot * NST + stage) * 2 + 1], st);
+  }
+};
+
+#define BEAM_TRY(expr)                                     \
+  do {                                                     \
+    if ((expr) != hipSuccess) return BEAM_MOE_ERR_HIP;     \
+  } while (0)
+
+// ---------------------------------------------------------------- pipelines
+int run_route(hipStream_t st, int64_t T, int H, int E, int groups, int topk_groups, int k, float scale,
+              const uint16_t* x, const uint16_t* wr, const float* off, int32_t* ids, float* w,
+              int32_t* user_counts, const Layout& L, char* ws, int slot) {
+  float* zpart = reinterpret_cast<float*>(ws + L.zpart);
+  {
+    StageScope sc(slot, ST_LOGITS, st);
+    BEAM_TRY(launch_router_logits(st, x, wr, zpart, (int)T, H, E, L.S));
+  }
+  {
+    StageScope sc(slot, ST_SELECT, st);
+    if (user_counts) BEAM_TRY(launch_fill_i32(st, user_counts, E, 0));
+    BEAM_TRY(launch_select(st, zpart, L.S, off, (int)T, E, groups, topk_groups, k, scale, ids, w,
+                           user_counts));
+  }
+  return BEAM_MOE_OK;
+}
+
+int run_permute(hipStream_t st, int64_t T, int E, int k, const int32_t* ids, int32_t* user_counts,
+                const Layout& L, char* ws, int32_t* offsets_out, int32_t* sorted_out, int32_t* rowof_out) {
+  const int64_t Tk = T * k;
+  BEAM_TRY(launch_permute(st, ids, Tk, k, E, reinterpret_cast<int32_t*>(ws + L.hist),
+                          reinterpret_cast<int32_t*>(ws + L.base), reinterpret_cast<int32_t*>(ws + L.counts),
+                          offsets_out, sorted_out, rowof_out, user_counts));
+  return BEAM_MOE_OK;
+}
+
+int run_forward(hipStream_t st, int64_t T, int H, int I, int E, int k, const uint16_t* x,
+                const int32_t* ids, const float* w, const uint16_t* wg, const uint16_t* wu,
+                const uint16_t* wd, uint16_t* y, int32_t* user_counts, const Layout& L, char* ws,
+                int slot, int num_cu) {
+  const int64_t Tk = T * k;
+  int32_t* counts = reinterpret_cast<int32_t*>(ws + L.counts);
+  int32_t* offsets = reinterpret_cast<int32_t*>(ws + L.offsets);
+  int32_t* sorted = reinterpret_cast<int32_t*>(ws + L.sorted);
+  int32_t* rowof = reinterpret_cast<int32_t*>(ws + L.rowof);
+  uint16_t* h = reinterpret_cast<uint16_t*>(ws + L.h);
+  float* o = reinterpret_cast<float*>(ws + L.o);
+  {
+    StageScope sc(slot, ST_PERMUTE, st);
+    int rc = run_permute(st, T, E, k, ids, user_counts, L, ws, offsets, sorted, rowof);
+    if (rc) return rc;
+  }
+  const bool stream = use_stream(T, k, E);
+  {
+    StageScope sc(slot, ST_GATEUP, st);
+    GroupedArgs a{x, sorted, wg, wu, counts, offsets, h, I, H, E, Tk};
+    BEAM_TRY(stream ? launch_gateup_stream(st, a, T, k) : launch_gateup_tiled(st, a, num_cu));
+  }
+  {
+    StageScope sc(slot, ST_DOWN, st);
+    GroupedArgs a{h, nullptr, wd, nullptr, counts, offsets, o, H, I, E, Tk};
+    BEAM_TRY(stream ? launch_down_stream(st, a, T, k) : launch_down_tiled(st, a, num_cu));
+  }
+  {
+    StageScope sc(slot, ST_COMBINE, st);
+    BEAM_TRY(launch_combine(st, o, rowof, w, (int)T, H, k, y));
+  }
+  return BEAM_MOE_OK;
+}
+
+}  // namespace
+
+// ============================================================================
+// Public entry points
+// ============================================================================
+extern "C" {
+
+const char* beam_moe_status_string(int status) {
+  switch (status) {
+    case BEAM_MOE_OK: return "ok";
+    case BEAM_MOE_ERR_INVALID_DIM: return "invalid dimension";
+    case BEAM_MOE_ERR_NULL_POINTER: return "null pointer";
+    case BEAM_MOE_ERR_MISALIGNED: return "pointer not 16-byte aligned";
+    case BEAM_MOE_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case BEAM_MOE_ERR_UNSUPPORTED_DEVICE: return "unsupported device (needs gfx950)";
+    case BEAM_MOE_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+const char* beam_moe_version(void) { return "0.1.0"; }
+
+size_t beam_moe_workspace_bytes(int64_t T, int H, int I, int E, int k) {
+  if (check_forward_dims(T, H, I, E, k) != BEAM_MOE_OK) return 0;
+  return layout(T, H, I, E, k).total;
+}
+
+int beam_moe_route(void* stream, int64_t T, int H, int E, int groups, int topk_groups, int k,
+                   float scale, const uint16_t* x, const uint16_t* w_router,
+                   const float* logit_offset, int32_t* topk_ids, float* topk_weights,
+                   int32_t* expert_counts, void* workspace, size_t workspace_bytes) {
+  int rc = check_route_dims(T, H, E, groups, topk_groups, k, scale);
+  if (rc) return rc;
+  if (T == 0) return BEAM_MOE_OK;
+  rc = check_ptrs({x, w_router, topk_ids, topk_weights, workspace}, {logit_offset, expert_counts});
+  if (rc) return rc;
+  const Layout L = route_layout(T, H, E);
+  if (workspace_bytes < L.total) return BEAM_MOE_ERR_WORKSPACE_TOO_SMALL;
+  int num_cu;
+  if ((rc = device_check(&num_cu))) return rc;
+  return run_route((hipStream_t)stream, T, H, E, groups, topk_groups, k, scale, x, w_router,
+                   logit_offset, topk_ids, topk_weights, expert_counts, L,
+                   static_cast<char*>(workspace), -1);
+}
+
+int beam_moe_permute(void* stream, int64_t T, int E, int k, const int32_t* topk_ids,
+                     int32_t* expert_counts, int32_t* expert_offsets, int32_t* sorted_tokens,
+                     int32_t* row_of, void* workspace, size_t workspace_bytes) {
+  if (T < 0 || T > kMaxT || E < 1 || E > kMaxE || k < 1 || k > kMaxK) return BEAM_MOE_ERR_INVALID_DIM;
+  if (T == 0) return BEAM_MOE_OK;
+  int rc = check_ptrs({topk_ids, expert_counts, expert_offsets, sorted_tokens, row_of, workspace}, {});
+  if (rc) return rc;
+  const Layout L = perm_layout(T, E, k);
+  if (workspace_bytes < L.total) return BEAM_MOE_ERR_WORKSPACE_TOO_SMALL;
+  int num_cu;
+  if ((rc = device_check(&num_cu))) return rc;
+  return run_permute((hipStream_t)stream, T, E, k, topk_ids, expert_counts, L,
+                     static_cast<char*>(workspace), expert_offsets, sorted_tokens, row_of);
+}
+
+int beam_moe_forward(void* stream, int64_t T, int H, int I, int E, int k, const uint16_t* x,
+                     const int32_t* topk_ids, const float* topk_weights, const uint16_t* w_gate,
+                     const uint16_t* w_up, const uint16_t* w_down, uint16_t* y,
+                     int32_t* expert_counts, void* workspace, size_t workspace_bytes) {
+  int rc = check_forward_dims(T, H, I, E, k);
+  if (rc) return rc;
+  if (T == 0) return BEAM_MOE_OK;
+  rc = check_ptrs({x, topk_ids, topk_weights, w_gate, w_up, w_down, y, workspace}, {expert_counts});
+  if (rc) return rc;
+  const Layout L = layout(T, H, I, E, k);
+  if (workspace_bytes < L.total) return BEAM_MOE_ERR_WORKSPACE_TOO_SMALL;
+  int num_cu;
+  if ((rc = device_check(&num_cu))) return rc;
+  const int slot = timer_claim();
+  return run_forward((hipStream_t)stream, T, H, I, E, k, x, topk_ids, topk_weights, w_gate, w_up,
+                     w_down, y, expert_counts, L, static_cast<char*>(workspace), slot, num_cu);
+}
+
+int beam_moe_block(void* stream, int64_t T, int H, int I, int E, int groups, int topk_groups, int k,
+                   float scale, const uint16_t* x, const uint16_t* w_router,
+                   const float* logit_offset, const uint16_t* w_gate, const uint16_t* w_up,
+                   const uint16_t* w_down, uint16_t* y, int32_t* topk_ids, float* topk_weights,
+                   int32_t* expert_counts, void* workspace, size_t workspace_bytes) {
+  int rc = check_route_dims(T, H, E, groups, topk_groups, k, scale);
+  if (rc) return rc;
+  if ((rc = check_forward_dims(T, H, I, E, k))) return rc;
+  if (T == 0) return BEAM_MOE_OK;
+  rc = check_ptrs({x, w_router, w_gate, w_up, w_down, y, workspace},
+                  {logit_offset, topk_ids, topk_weights, expert_counts});
+  if (rc) return rc;
+  const Layout L = layout(T, H, I, E, k);
+  if (workspace_bytes < L.total) return BEAM_MOE_ERR_WORKSPACE_TOO_SMALL;
+  int num_cu;
+  if ((rc = device_check(&num_cu))) return rc;
+  char* ws = static_cast<char*>(workspace);
+  int32_t* ids = topk_ids ? topk_ids : reinterpret_cast<int32_t*>(ws + L.ids);
+  float* w = topk_weights ? topk_weights : reinterpret_cast<float*>(ws + L.w);
+  hipStream_t st = (hipStream_t)stream;
+  const int slot = timer_claim();
+  rc = run_route(st, T, H, E, groups, topk_groups, k, scale, x, w_router, logit_offset, ids, w,
+                 nullptr, L, ws, slot);
+  if (rc) return rc;
+  return run_forward(st, T, H, I, E, k, x, ids, w, w_gate, w_up, w_down, y, expert_counts, L, ws,
+                     slot, num_cu);
+}
+
+int beam_moe_stream_init(void* stream, int64_t T, int H, const uint16_t* x, float* stream_out) {
+  if (T < 0 || T > kMaxT || bad_dim64(H)) return BEAM_MOE_ERR_INVALID_DIM;
+  if (T == 0) return BEAM_MOE_OK;
+  int rc = check_ptrs({x, stream_out}, {});
+  if (rc) return rc;
+  int num_cu;
+  if ((rc = device_check(&num_cu))) return rc;
+  BEAM_TRY(launch_stream_init((hipStream_t)stream, x, stream_out, T, H));
+  return BEAM_MOE_OK;
+}
+
+int beam_moe_rmsnorm(void* stream, int64_t T, int H, float eps, const float* in, uint16_t* out) {
+  if (T < 0 || T > kMaxT || bad_dim64(H) || !(eps >= 0.f) || !isfinite(eps)) return BEAM_MOE_ERR_INVALID_DIM;
+  if (T == 0) return BEAM_MOE_OK;
+  int rc = check_ptrs({in, out}, {});
+  if (rc) return rc;
+  int num_cu;
+  if ((rc = device_check(&num_cu))) return rc;
+  BEAM_TRY(launch_rmsnorm((hipStream_t)stream, in, out, T, H, eps));
+  return BEAM_MOE_OK;
+}
+
+int beam_moe_residual_update(void* stream, int64_t T, int H, float eps, int step, const uint16_t* y,
+                             float* stream_io) {
+  if (T < 0 || T > kMaxT || bad_dim64(H) || step < 2 || !(eps >= 0.f) || !isfinite(eps))
+    return BEAM_MOE_ERR_INVALID_DIM;
+  if (T == 0) return BEAM_MOE_OK;
+  int rc = check_ptrs({y, stream_io}, {});
+  if (rc) return rc;
+  int num_cu;
+  if ((rc = device_check(&num_cu))) return rc;
+  BEAM_TRY(launch_residual((hipStream_t)stream, y, stream_io, T, H, eps, step));
+  return BEAM_MOE_OK;
+}
+
+int beam_moe_sublayer(void* stream, int64_t T, int H, int I, int E, int groups, int topk_groups, int k,
+                      float scale, float eps, int step, float* stream_io, const uint16_t* w_router,
+                      const uint16_t* w_gate, const uint16_t* w_up, const uint16_t* w_down,
+                      uint16_t* moe_input, uint16_t* moe_output, int32_t* topk_ids,
+                      float* topk_weights, int32_t* expert_counts, void* workspace,
+                      size_t workspace_bytes) {
+  int rc = check_route_dims(T, H, E, groups, topk_groups, k, scale);
+  if (rc) return rc;
+  if ((rc = check_forward_dims(T, H, I, E, k))) return rc;
+  if (step < 2 || !(eps >= 0.f) || !isfinite(eps)) return BEAM_MOE_ERR_INVALID_DIM;
+  if (T == 0) return BEAM_MOE_OK;
+  rc = check_ptrs({stream_io, w_router, w_gate, w_up, w_down, workspace},
+                  {moe_input, moe_output, topk_ids, topk_weights, expert_counts});
+  if (rc) return rc;
+  const Layout L = layout(T, H, I, E, k);
+  if (workspace_bytes < L.total) return BEAM_MOE_ERR_WORKSPACE_TOO_SMALL;
+  int num_cu;
+  if ((rc = device_check(&num_cu))) return rc;
+  char* ws = static_cast<char*>(workspace);
+  hipStream_t st = (hipStream_t)stream;
+  uint16_t* xin = moe_input ? moe_input : reinterpret_cast<uint16_t*>(ws + L.xin);
+  uint16_t* yb = moe_output ? moe_output : reinterpret_cast<uint16_t*>(ws + L.y);
+  int32_t* ids = topk_ids ? topk_ids : reinterpret_cast<int32_t*>(ws + L.ids);
+  float* w = topk_weights ? topk_weights : reinterpret_cast<float*>(ws + L.w);
+  BEAM_TRY(launch_rmsnorm(st, stream_io, xin, T, H, eps));
+  const int slot = timer_claim();
+  rc = run_route(st, T, H, E, groups, topk_groups, k, scale, xin, w_router, nullptr, ids, w, nullptr,
+                 L, ws, slot);
+  if (rc) return rc;
+  rc = run_forward(st, T, H, I, E, k, xin, ids, w, w_gate, w_up, w_down, yb, expert_counts, L, ws,
+                   slot, num_cu);
+  if (rc) return rc;
+  BEAM_TRY(launch_residual(st, yb, stream_io, T, H, eps, step));
+  return BEAM_MOE_OK;
+}
+
+// ---------------------------------------------------------------- schedule / timer
+int beam_moe_set_schedule(int mode) {
+  if (mode < 0 || mode > 2) return BEAM_MOE_ERR_INVALID_DIM;
+  g_schedule.store(mode, std::memory_order_relaxed);
+  return BEAM_MOE_OK;
+}
+
+int beam_moe_stage_count(void) { return NST; }
+
+const char* beam_moe_stage_name(int stage) {
+  return (stage >= 0 && stage < NST) ? kStageNames[stage] : "";
+}
+
+int beam_moe_timer_begin(int max_calls) {
+  if (max_calls < 1 || max_calls > 100000) return BEAM_MOE_ERR_INVALID_DIM;
+  std::lock_guard<std::mutex> lk(g_timer.mu);
+  if (g_timer.on) return BEAM_MOE_ERR_INVALID_DIM;
+  g_timer.ev.assign((size_t)max_calls * NST * 2, nullptr);
+  g_timer.used.assign((size_t)max_calls * NST, 0);
+  for (auto& e : g_timer.ev)
+    if (hipEventCreate(&e) != hipSuccess) return BEAM_MOE_ERR_HIP;
+  g_timer.max_calls = max_calls;
+  g_timer.n_calls = 0;
+  g_timer.on = true;
+  return BEAM_MOE_OK;
+}
+
+int beam_moe_timer_end(double* stage_ms, int n_stages, int* n_calls) {
+  if (!stage_ms || !n_calls) return BEAM_MOE_ERR_NULL_POINTER;
+  if (n_stages < NST) return BEAM_MOE_ERR_INVALID_DIM;
+  std::lock_guard<std::mutex> lk(g_timer.mu);
+  if (!g_timer.on) return BEAM_MOE_ERR_INVALID_DIM;
+  int rc = BEAM_MOE_OK;
+  for (int s = 0; s < n_stages; ++s) stage_ms[s] = 0.0;
+  for (int c = 0; c < g_timer.n_calls; ++c)
+    for (int s = 0; s < NST; ++s) {
+      if (!g_timer.used[(size_t)c * NST + s]) continue;
+      hipEvent_t a = g_timer.ev[(size_t)(c * NST + s) * 2], b = g_timer.ev[(size_t)(c * NST + s) * 2 + 1];
+      float ms = 0.f;
+      if (hipEventSynchronize(b) != hipSuccess || hipEventElapsedTime(&ms, a, b) != hipSuccess) {
+        rc = BEAM_MOE_ERR_HIP;
+        continue;
+      }
+      stage_ms[s] += ms;
+    }
+  *n_calls = g_timer.n_calls;
+  for (auto& e : g_timer.ev)
+    if (e) (void)hipEventDestroy(e);
+  g_timer.ev.clear();
+  g_timer.used.clear();
+  g_timer.on = false;
+  return rc;
+}
+
+}  // extern "C"

@@ -1,0 +1,45 @@
+// Shared device helpers for the gfx950 kernels of libbeam_moe.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace beam {
+
+typedef __bf16 bf16x8 __attribute__((__vector_size__(8 * sizeof(__bf16))));
+typedef float f32x4 __attribute__((__vector_size__(4 * sizeof(float))));
+
+// bf16 bit pattern -> fp32 (exact).
+__device__ __forceinline__ float bf16_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+
+// fp32 -> bf16 bit pattern, round to nearest, ties to even.  Adding 0x7fff
+// plus the lowest kept bit carries into the kept bits exactly when the
+// dropped half is above one half ulp, or equal to it with an odd kept part.
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;  // NaN stays NaN
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+// 16-byte global load / store helpers.
+__device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
+__device__ __forceinline__ void st16(void* p, uint4 v) { *reinterpret_cast<uint4*>(p) = v; }
+
+__device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+// One 16x16x32 bf16 MFMA (gfx950): D = A(16x32) * B(32x16) + C.
+// Lane l supplies A row (l % 16) and B column (l % 16), each with the 8
+// k-values of its 16-byte operand; the k-slot each lane group (l / 16)
+// stands for only needs to agree between A and B, since the products are
+// summed.  The result holds rows 4*(l/16) .. 4*(l/16)+3 of column l % 16.
+__device__ __forceinline__ f32x4 mfma16(uint4 a, uint4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
+}
+
+// SiLU(g) * u in fp32: g / (1 + exp(-g)) * u.
+__device__ __forceinline__ float swiglu(float g, float u) { return g / (1.0f + expf(-g)) * u; }
+
+__device__ __forceinline__ int wave_lane() { return threadIdx.x & 63; }
+
+}  // namespace beam
