@@ -173,9 +173,11 @@ def main():
     roof["avg_launch_ms"] = round(gu_ms, 5)
 
     if args.copy_probe:
-        a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        # plain elementwise copy of known size: reads 1 GiB, writes 1 GiB
+        a = torch.ones(1 << 28, dtype=torch.float32, device=dev)
         b = torch.empty_like(a)
-        b.copy_(a)
+        for _ in range(2):
+            torch.neg(a, out=b)
         torch.cuda.synchronize()
         del a, b
 
@@ -217,7 +219,7 @@ def cpu_baseline(args, shape, x, wr, wg, wu, wd, off):
     import oracle as O
     from moe_inputs import bf16_bits
 
-    n = args.cpu_sample_tokens or {"decode": 4, "tiny": 128}.get(args.workload, 4)
+    n = args.cpu_sample_tokens or {"decode": 64, "tiny": 128}.get(args.workload, 16)
     n = min(n, shape.T)
     xb = bf16_bits(x[:n])
     wrb = bf16_bits(wr)
