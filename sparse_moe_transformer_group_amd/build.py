@@ -16,6 +16,7 @@ CSRC = os.path.join(PKG_DIR, "csrc")
 LIB_NAME = "libbeam_moe.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
 BUILD_DIR = os.path.join(PKG_DIR, "_build")
+INCLUDE_DIR = os.path.join(os.path.dirname(PKG_DIR), "include")   # public C header
 
 ARCH = "gfx950"
 COMMON_FLAGS = [
@@ -34,7 +35,7 @@ def hipcc() -> str:
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
-    cmd = [hipcc(), *COMMON_FLAGS, "-c", src, "-o", obj]
+    cmd = [hipcc(), *COMMON_FLAGS, f"-I{INCLUDE_DIR}", "-c", src, "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{res.stdout}\n{res.stderr}")

@@ -7,7 +7,7 @@
 #include <mutex>
 #include <vector>
 
-#include "../../include/beam_moe.h"
+#include "beam_moe.h"
 #include "common.h"
 #include "kernels.h"
 
@@ -138,7 +138,15 @@ int device_check(int* num_cu) {
 // ---------------------------------------------------------------- schedule knob
 std::atomic<int> g_schedule{0};  // 0 auto, 1 stream, 2 tiled
 
-bool use_stream(int64_t T, int k, int E) {
+// The tiled kernels address one expert's weight matrix and the activation
+// tensor with 32-bit buffer offsets; larger tensors take the streaming path.
+bool tiled_fits(int64_t T, int H, int I, int k) {
+  const int64_t lim = int64_t(1) << 31;
+  return (int64_t)H * I * 2 < lim && T * H * 2 < lim && T * k * I * 2 < lim;
+}
+
+bool use_stream(int64_t T, int H, int I, int k, int E) {
+  if (!tiled_fits(T, H, I, k)) return true;
   const int m = g_schedule.load(std::memory_order_relaxed);
   if (m == 1) return true;
   if (m == 2) return false;
@@ -225,7 +233,7 @@ int run_forward(hipStream_t st, int64_t T, int H, int I, int E, int k, const uin
     int rc = run_permute(st, T, E, k, ids, user_counts, L, ws, offsets, sorted, rowof);
     if (rc) return rc;
   }
-  const bool stream = use_stream(T, k, E);
+  const bool stream = use_stream(T, H, I, k, E);
   {
     StageScope sc(slot, ST_GATEUP, st);
     GroupedArgs a{x, sorted, wg, wu, counts, offsets, h, I, H, E, Tk};

@@ -14,41 +14,48 @@
 namespace beam {
 
 // y[t, :] = bf16( sum_j w[t,j] * o[row_of[t*k+j], :] ): FP32 fused multiply-adds
-// in slot order j = 0..k-1, one rounding at the end.  One workgroup per token,
-// 16-byte loads of the FP32 partial rows.
+// in slot order j = 0..k-1, one rounding at the end.  Workgroup (c, t) covers
+// 1024 columns of token t; each thread issues the loads of all its slots
+// (16-byte loads of the FP32 partial rows) before summing them in order.
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ o,
                                                       const int32_t* __restrict__ row_of,
                                                       const float* __restrict__ w, int H, int k,
                                                       uint16_t* __restrict__ y) {
-  __shared__ int s_row[32];
-  __shared__ float s_w[32];
-  const int64_t t = blockIdx.x;
-  if (threadIdx.x < k) {
-    s_row[threadIdx.x] = row_of[t * k + threadIdx.x];
-    s_w[threadIdx.x] = w[t * k + threadIdx.x];
-  }
-  __syncthreads();
-  for (int c = threadIdx.x * 4; c < H; c += 256 * 4) {
-    float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
-    for (int j = 0; j < k; ++j) {
-      const int row = s_row[j];
-      if (row < 0) continue;
-      const f32x4 v = *reinterpret_cast<const f32x4*>(o + (int64_t)row * H + c);
-      const float wj = s_w[j];
-      a0 = fmaf(wj, v[0], a0);
-      a1 = fmaf(wj, v[1], a1);
-      a2 = fmaf(wj, v[2], a2);
-      a3 = fmaf(wj, v[3], a3);
+  const int64_t t = blockIdx.y;
+  const int c = (blockIdx.x * 256 + threadIdx.x) * 4;
+  if (c >= H) return;
+  float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+  for (int j0 = 0; j0 < k; j0 += 8) {
+    f32x4 v[8];
+    float wj[8];
+    bool ok[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int j = j0 + u;
+      const int row = (j < k) ? row_of[t * k + j] : -1;
+      ok[u] = row >= 0;  // a dropped slot (id outside [0, E)) contributes nothing
+      wj[u] = ok[u] ? w[t * k + j] : 0.f;
+      v[u] = ok[u] ? *reinterpret_cast<const f32x4*>(o + (int64_t)row * H + c)
+                   : f32x4{0.f, 0.f, 0.f, 0.f};
     }
-    const uint2 pk = make_uint2(f32_to_bf16_rne(a0) | (f32_to_bf16_rne(a1) << 16),
-                                f32_to_bf16_rne(a2) | (f32_to_bf16_rne(a3) << 16));
-    *reinterpret_cast<uint2*>(y + t * H + c) = pk;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      if (!ok[u]) continue;
+      a0 = fmaf(wj[u], v[u][0], a0);
+      a1 = fmaf(wj[u], v[u][1], a1);
+      a2 = fmaf(wj[u], v[u][2], a2);
+      a3 = fmaf(wj[u], v[u][3], a3);
+    }
   }
+  const uint2 pk = make_uint2(f32_to_bf16_rne(a0) | (f32_to_bf16_rne(a1) << 16),
+                              f32_to_bf16_rne(a2) | (f32_to_bf16_rne(a3) << 16));
+  *reinterpret_cast<uint2*>(y + t * H + c) = pk;
 }
 
 hipError_t launch_combine(hipStream_t st, const float* o, const int32_t* row_of, const float* w, int T,
                           int H, int k, uint16_t* y) {
-  hipLaunchKernelGGL(combine_kernel, dim3(T), dim3(256), 0, st, o, row_of, w, H, k, y);
+  dim3 grid((H + 1023) / 1024, T);
+  hipLaunchKernelGGL(combine_kernel, grid, dim3(256), 0, st, o, row_of, w, H, k, y);
   return hipGetLastError();
 }
 

@@ -133,11 +133,80 @@ __global__ __launch_bounds__(256) void perm_scatter_kernel(const int32_t* __rest
   }
 }
 
+// Whole permutation in one workgroup when all assignments fit one chunk
+// (decode-size batches): histogram, scan and ranked scatter without the two
+// extra launches.  Same results as the three-kernel path.
+__global__ __launch_bounds__(256) void perm_single_kernel(const int32_t* __restrict__ ids, int Tk, int k,
+                                                          int E, int32_t* __restrict__ counts,
+                                                          int32_t* __restrict__ offsets,
+                                                          int32_t* __restrict__ sorted_tokens,
+                                                          int32_t* __restrict__ row_of,
+                                                          int32_t* __restrict__ user_counts) {
+  __shared__ uint32_t mask[kMaxE * kMaskWords];
+  __shared__ int hist[kMaxE];
+  __shared__ int scan[kMaxE];
+  for (int i = threadIdx.x; i < E * kMaskWords; i += 256) mask[i] = 0u;
+  for (int e = threadIdx.x; e < E; e += 256) hist[e] = 0;
+  __syncthreads();
+  int ev[kPermChunk / 256];
+#pragma unroll
+  for (int r = 0; r < kPermChunk / 256; ++r) {
+    const int i = threadIdx.x + 256 * r;
+    const int e = (i < Tk) ? ids[i] : -1;
+    ev[r] = e;
+    if ((unsigned)e < (unsigned)E) {
+      atomicOr(&mask[e * kMaskWords + (i >> 5)], 1u << (i & 31));
+      atomicAdd(&hist[e], 1);
+    }
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += 256) scan[e] = hist[e];
+  __syncthreads();
+  for (int off = 1; off < E; off <<= 1) {  // inclusive Hillis-Steele scan
+    int v0 = 0, v1 = 0;
+    const int e0 = threadIdx.x, e1 = threadIdx.x + 256;
+    if (e0 < E && e0 >= off) v0 = scan[e0 - off];
+    if (e1 < E && e1 >= off) v1 = scan[e1 - off];
+    __syncthreads();
+    if (e0 < E) scan[e0] += v0;
+    if (e1 < E) scan[e1] += v1;
+    __syncthreads();
+  }
+  for (int e = threadIdx.x; e < E; e += 256) {
+    counts[e] = hist[e];
+    offsets[e] = scan[e] - hist[e];
+    if (user_counts) user_counts[e] = hist[e];
+    if (e == E - 1) offsets[E] = scan[E - 1];
+  }
+#pragma unroll
+  for (int r = 0; r < kPermChunk / 256; ++r) {
+    const int i = threadIdx.x + 256 * r;
+    if (i >= Tk) continue;
+    const int e = ev[r];
+    if ((unsigned)e >= (unsigned)E) {
+      row_of[i] = -1;
+      continue;
+    }
+    const uint32_t* m = mask + e * kMaskWords;
+    const int w = i >> 5;
+    int rank = __popc(m[w] & ((1u << (i & 31)) - 1u));
+    for (int j = 0; j < w; ++j) rank += __popc(m[j]);
+    const int pos = scan[e] - hist[e] + rank;
+    sorted_tokens[pos] = i / k;
+    row_of[i] = pos;
+  }
+}
+
 hipError_t launch_permute(hipStream_t st, const int32_t* ids, int64_t Tk, int k, int E,
                           int32_t* block_hist, int32_t* block_base, int32_t* counts,
                           int32_t* offsets, int32_t* sorted_tokens, int32_t* row_of,
                           int32_t* user_counts) {
   const int64_t NB = perm_blocks(Tk);
+  if (NB == 1) {
+    hipLaunchKernelGGL(perm_single_kernel, dim3(1), dim3(256), 0, st, ids, (int)Tk, k, E, counts,
+                       offsets, sorted_tokens, row_of, user_counts);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL(perm_hist_kernel, dim3((unsigned)NB), dim3(256), 0, st, ids, Tk, E, block_hist);
   hipLaunchKernelGGL(perm_scan_kernel, dim3(1), dim3(1024), 0, st, block_hist, (int)NB, E, block_base,
                      counts, offsets, user_counts);

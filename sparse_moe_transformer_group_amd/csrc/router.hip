@@ -49,20 +49,31 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const uint16_t* __re
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-#pragma unroll 2
-  for (int kk = kb; kk < ke; ++kk) {
-    const int k = kk * 32;
-    uint4 a[4], b[4];
+  // software-pipelined: the next k-step's operands are in flight while the
+  // current one is multiplied
+  uint4 a[2][4], b[2][4];
+  auto load = [&](int buf, int kk) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      a[i] = ld16(ap[i] + k);
-      b[i] = ld16(bp[i] + k);
+      a[buf][i] = ld16(ap[i] + kk * 32);
+      b[buf][i] = ld16(bp[i] + kk * 32);
     }
+  };
+  auto mult = [&](int buf) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] = mfma16(a[i], b[j], acc[i][j]);
+      for (int j = 0; j < 4; ++j) acc[i][j] = mfma16(a[buf][i], b[buf][j], acc[i][j]);
+  };
+  if (kb < ke) load(0, kb);
+  int kk = kb;
+  for (; kk + 2 <= ke; kk += 2) {
+    load(1, kk + 1);
+    mult(0);
+    if (kk + 2 < ke) load(0, kk + 2);
+    mult(1);
   }
+  if (kk < ke) mult(0);
 
   float* zs = zpart + (int64_t)s * T * E;
 #pragma unroll
@@ -157,8 +168,16 @@ __global__ __launch_bounds__(256) void select_kernel(const float* __restrict__ z
     float z = 0.f;
     if (e < E) {
       const float* zp = zpart + (int64_t)t * E + e;
-      z = zp[0];
-      for (int s = 1; s < S; ++s) z += zp[(int64_t)s * T * E];
+      const int64_t sstride = (int64_t)T * E;
+      // batches of 8 independent loads, added strictly in slice order
+      for (int s0 = 0; s0 < S; s0 += 8) {
+        float v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = (s0 + u < S) ? zp[(s0 + u) * sstride] : 0.f;
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+          if (s0 + u < S) z = (s0 + u == 0) ? v[u] : z + v[u];
+      }
       if (offset) z += offset[e];
       sc[i] = 1.0f / (1.0f + expf(-z));
     } else {
