@@ -34,7 +34,11 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 METRIC = "MoE-layer tokens/s at H=5120,E=256,k=8; % of peak MFMA / HBM GB/s"
-GEMM_SRC = os.path.join(ROOT, "sparse_moe_transformer_group_amd", "csrc", "gemm.hip")
+CSRC = os.path.join(ROOT, "sparse_moe_transformer_group_amd", "csrc")
+# source file of each gate/up schedule (the stream kernel serves decode-size
+# batches, the tiled kernel prefill sizes)
+GEMM_SRC = {"stream": os.path.join(CSRC, "gemm_stream.hip"),
+            "tiled": os.path.join(CSRC, "gemm_tiled.hip")}
 
 
 def parse():
@@ -51,12 +55,12 @@ def parse():
     return p.parse_args()
 
 
-def kernel_hash():
-    with open(GEMM_SRC, "rb") as f:
+def kernel_hash(schedule):
+    with open(GEMM_SRC[schedule], "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def measured_traffic(workload):
+def measured_traffic(workload, schedule):
     """HBM bytes per launch of the gate/up kernel from the committed counter
     summary, if it was taken on this kernel source."""
     path = os.path.join(ROOT, "profiles", f"traffic_gateup_{workload}.json")
@@ -64,7 +68,7 @@ def measured_traffic(workload):
         return None
     with open(path) as f:
         d = json.load(f)
-    if d.get("gemm_source_sha256_16") != kernel_hash():
+    if d.get("gemm_source_sha256_16") != kernel_hash(schedule):
         return None
     return d.get("bytes_per_launch")
 
@@ -166,8 +170,9 @@ def main():
         ach = gu_flops / (gu_ms * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4)}
-    roof["traffic"] = measured_traffic(args.workload)
-    roof["kernel"] = "grouped_stream_kernel<2,1,*> (gate/up)" if T * k <= 32 * E else \
+    schedule = "stream" if T * k <= 32 * E else "tiled"
+    roof["traffic"] = measured_traffic(args.workload, schedule)
+    roof["kernel"] = "grouped_stream_kernel<2,1,*> (gate/up)" if schedule == "stream" else \
         "grouped_tiled_kernel<2,...> (gate/up)"
     roof["algorithmic_per_launch"] = {"bytes": int(gu_bytes), "flops": int(gu_flops)}
     roof["avg_launch_ms"] = round(gu_ms, 5)

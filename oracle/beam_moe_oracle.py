@@ -23,7 +23,7 @@ What the pages fix, restated:
     embedding as step 1 and at step k keeps sqrt((k-1)/k) of the stream and
     adds 1/sqrt(k) of the sublayer output.
 
-Readings where the pages are silent (each one is listed in the design doc):
+Readings where the pages are silent:
   groups are contiguous blocks of E/groups experts; exact ties go to the lower
   index; normalisation is over the k selected sigmoid scores with no epsilon,
   and the 2.5 is folded into the returned weights; no router or expert bias;

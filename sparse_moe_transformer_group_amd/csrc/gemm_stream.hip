@@ -1,0 +1,217 @@
+// Grouped expert GEMMs of the Beam MoE block on gfx950 MFMA.
+//
+// Every expert is a SwiGLU MLP, hidden 5120 -> intermediate 2560 -> hidden
+// (page "Willkommen Beam: ein offenes 501B-Modell, das Sie besitzen, anpassen
+// und skalieren können", section "Mixture of Experts"); the SwiGLU product is
+// formed in FP32 (same page, section "Residual Stream").
+//
+//   gate/up:  h[row, n] = bf16( SiLU(sum_k Wg[e,n,k] x[tok,k]) * sum_k Wu[e,n,k] x[tok,k] )
+//   down:     o[row, n] = sum_k Wd[e,n,k] h[row,k]                       (FP32 out)
+// where row runs over the expert-major rows of expert e and tok is the token
+// of that row.  Weights are the MFMA A operand, tokens the B operand; both
+// are K-contiguous.
+//
+// This file: the stream schedule, for decode-size batches (a handful of
+// tokens per expert).  Bound by reading the active experts' weights once
+// from HBM.  Each wave streams its own weight rows with coalesced
+// nontemporal loads (16 lanes cover a 256-byte row segment; each byte is
+// used once), re-lays them out through a wave-private LDS tile into the
+// 16x16x32 MFMA operand layout, and multiplies them with the expert's tokens
+// (up to 16*MT MFMA columns, read from L2).  No workgroup barriers.
+// The prefill-size schedule is in gemm_tiled.hip.
+#include <type_traits>
+
+#include "common.h"
+#include "kernels.h"
+
+namespace beam {
+
+// ===========================================================================
+// Stream schedule
+// ===========================================================================
+// MAT = 2: gate+up with SwiGLU epilogue (bf16 out); MAT = 1: down (fp32 out).
+// RB  = 16-row weight blocks per wave per matrix; MT = 16-token tiles held.
+//
+// Each wave owns ROWS = MAT*RB*16 weight rows and walks K in steps of 128
+// (256 bytes per row).  A step's weight slab (ROWS x 256 B) is read with
+// fully coalesced nontemporal 16-byte loads, 16 lanes per row segment, so
+// every load instruction covers whole cache lines; it is then re-laid into
+// the MFMA operand layout through a wave-private LDS tile (16-byte chunks
+// XOR-swizzled by row, conflict-free).  The next step's slab is in flight
+// while the current one is multiplied.  Within a step, MFMA j (0..3) takes
+// 16-byte chunk 4j+q of the row segment for lane group q; the token operand
+// uses the same k mapping.
+template <int MAT, int RB, int MT>
+__global__ __launch_bounds__(256) void grouped_stream_kernel(GroupedArgs a) {
+  constexpr int ROWS = MAT * RB * 16;
+  constexpr int LD = ROWS / 4;  // 16-byte loads per lane per step (4 rows per wave load)
+  __shared__ __attribute__((aligned(16))) unsigned char lds[4][ROWS * 256];
+
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int r = lane & 15, q = lane >> 4;
+  const int e = blockIdx.y;
+  const int n_e = a.counts[e];
+  if (n_e <= 0) return;
+  const int f0 = (blockIdx.x * 4 + wave) * (RB * 16);
+  if (f0 >= a.N) return;  // no workgroup barriers in this kernel
+  const int row0 = a.offsets[e];
+  const int N = a.N, K = a.K;
+  unsigned char* tile = lds[wave];
+
+  // Load slot i of this lane: wave row rw = 4i + lane/16, 16-byte chunk lane%16.
+  const uint16_t* lp[LD];
+  int lo[LD];
+#pragma unroll
+  for (int i = 0; i < LD; ++i) {
+    const int rw = 4 * i + (lane >> 4);
+    const int c = lane & 15;
+    const int m = rw / (RB * 16);
+    const int fr = rw % (RB * 16);
+    const int f = min(f0 + fr, N - 1);
+    const uint16_t* base = (m == 0) ? a.w0 : a.w1;
+    lp[i] = base + ((int64_t)e * N + f) * K + c * 8;
+    lo[i] = rw * 256 + ((c ^ (rw & 15)) << 4);
+  }
+
+  for (int c0 = 0; c0 < n_e; c0 += 16 * MT) {
+    const uint16_t* bp[MT];
+    bool bv[MT];
+#pragma unroll
+    for (int j = 0; j < MT; ++j) {
+      const int tok = c0 + 16 * j + r;
+      bv[j] = tok < n_e;
+      const int rr = row0 + (bv[j] ? tok : 0);
+      const int64_t src = a.sorted_tokens ? (int64_t)a.sorted_tokens[rr] : (int64_t)rr;
+      bp[j] = a.act + src * K + q * 8;
+    }
+    f32x4 acc[MAT][RB][MT];
+#pragma unroll
+    for (int m = 0; m < MAT; ++m)
+#pragma unroll
+      for (int i = 0; i < RB; ++i)
+#pragma unroll
+        for (int j = 0; j < MT; ++j) acc[m][i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    const int nsteps = K / 128;  // K is a multiple of 64; a 64-wide tail is handled below
+    uint4 R[LD];
+    uint4 B[2][MT][4];
+    auto load_w = [&](int ks) {
+#pragma unroll
+      for (int i = 0; i < LD; ++i) R[i] = ld16_nt(lp[i] + ks * 128);
+    };
+    auto load_b = [&](int buf, int ks) {
+#pragma unroll
+      for (int t = 0; t < MT; ++t)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          B[buf][t][j] = bv[t] ? ld16(bp[t] + ks * 128 + j * 32) : make_uint4(0u, 0u, 0u, 0u);
+    };
+    auto step = [&](int buf, int ks) {
+      // slab of step ks: registers -> LDS tile, then prefetch step ks+1
+#pragma unroll
+      for (int i = 0; i < LD; ++i) st16(tile + lo[i], R[i]);
+      __builtin_amdgcn_wave_barrier();
+      if (ks + 1 < nsteps) {
+        load_w(ks + 1);
+        load_b(buf ^ 1, ks + 1);
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+#pragma unroll
+        for (int m = 0; m < MAT; ++m)
+#pragma unroll
+          for (int i = 0; i < RB; ++i) {
+            const int rw = m * RB * 16 + i * 16 + r;
+            const uint4 av = *reinterpret_cast<const uint4*>(tile + rw * 256 + (((4 * j + q) ^ r) << 4));
+#pragma unroll
+            for (int t = 0; t < MT; ++t) acc[m][i][t] = mfma16(av, B[buf][t][j], acc[m][i][t]);
+          }
+      }
+      __builtin_amdgcn_wave_barrier();
+    };
+
+    if (nsteps > 0) {
+      load_w(0);
+      load_b(0, 0);
+    }
+    int ks = 0;
+    for (; ks + 2 <= nsteps; ks += 2) {
+      step(0, ks);
+      step(1, ks + 1);
+    }
+    if (ks < nsteps) step(0, ks);
+
+    if (K % 128) {
+      // 64-wide tail: ordinary loads straight into the operand layout; lane
+      // group q covers k in [kt + 16q, kt + 16q + 16) as two 8-wide pieces.
+      const int kt = nsteps * 128;
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        uint4 bt[MT];
+#pragma unroll
+        for (int t = 0; t < MT; ++t)
+          bt[t] = bv[t] ? ld16(bp[t] - q * 8 + kt + q * 16 + c * 8) : make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+        for (int m = 0; m < MAT; ++m)
+#pragma unroll
+          for (int i = 0; i < RB; ++i) {
+            const int f = min(f0 + 16 * i + r, N - 1);
+            const uint16_t* base = (m == 0) ? a.w0 : a.w1;
+            const uint4 at = ld16(base + ((int64_t)e * N + f) * K + kt + q * 16 + c * 8);
+#pragma unroll
+            for (int t = 0; t < MT; ++t) acc[m][i][t] = mfma16(at, bt[t], acc[m][i][t]);
+          }
+      }
+    }
+
+    // Epilogue: lane holds features f0+16i+4q+c (c = 0..3) of token c0+16t+r.
+#pragma unroll
+    for (int i = 0; i < RB; ++i) {
+      const int f = f0 + 16 * i + 4 * q;
+      if (f >= N) continue;
+#pragma unroll
+      for (int t = 0; t < MT; ++t) {
+        const int tok = c0 + 16 * t + r;
+        if (tok >= n_e) continue;
+        const int64_t row = row0 + tok;
+        if constexpr (MAT == 2) {
+          uint32_t p[4];
+#pragma unroll
+          for (int c = 0; c < 4; ++c) p[c] = f32_to_bf16_rne(swiglu(acc[0][i][t][c], acc[1][i][t][c]));
+          uint2 v = make_uint2(p[0] | (p[1] << 16), p[2] | (p[3] << 16));
+          *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + row * N + f) = v;
+        } else {
+          *reinterpret_cast<f32x4*>(static_cast<float*>(a.out) + row * N + f) = acc[0][i][t];
+        }
+      }
+    }
+  }
+}
+
+// Token tiles held per pass: enough for the expected tokens per expert, so
+// that the weights are usually streamed exactly once.
+static int stream_mt(int64_t T, int k, int E) {
+  const double avg = (double)T * k / E;
+  if (avg <= 6.0) return 1;
+  if (avg <= 16.0) return 2;
+  return 4;
+}
+
+template <int MAT, int RB>
+static hipError_t launch_stream(hipStream_t st, const GroupedArgs& a, int mt) {
+  dim3 grid((a.N + 4 * RB * 16 - 1) / (4 * RB * 16), a.E), block(256);
+  if (mt == 1) hipLaunchKernelGGL((grouped_stream_kernel<MAT, RB, 1>), grid, block, 0, st, a);
+  else if (mt == 2) hipLaunchKernelGGL((grouped_stream_kernel<MAT, RB, 2>), grid, block, 0, st, a);
+  else hipLaunchKernelGGL((grouped_stream_kernel<MAT, RB, 4>), grid, block, 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_gateup_stream(hipStream_t st, const GroupedArgs& a, int64_t T, int k) {
+  return launch_stream<2, 1>(st, a, stream_mt(T, k, a.E));
+}
+
+hipError_t launch_down_stream(hipStream_t st, const GroupedArgs& a, int64_t T, int k) {
+  return launch_stream<1, 2>(st, a, stream_mt(T, k, a.E));
+}
+
+}  // namespace beam
