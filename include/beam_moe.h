@@ -67,6 +67,30 @@ const char* beam_moe_version(void);
 size_t beam_moe_workspace_bytes(int64_t T, int H, int I, int E, int k);
 
 /*
+ * Packed expert weights.  forward, block and sublayer read the expert weight
+ * matrices in a packed block layout, produced once (at model load) by
+ * beam_moe_pack_weights from the nn.Linear layout W[e][n][k] (k contiguous):
+ *   - each expert matrix W[e] (N x K) becomes ceil(N/128) row blocks x K/32
+ *     k-blocks of 128 rows x 32 k = 8192 bytes; block (rb, kb) starts at
+ *     byte (rb * K/32 + kb) * 8192 of the expert; experts follow each other,
+ *     each taking beam_moe_packed_weight_bytes(N, K) bytes;
+ *   - row j (0..127) of a block takes 64 bytes at byte j*64; its 16-byte
+ *     chunk c (0..3), holding k = kb*32 + 8c .. kb*32 + 8c + 7, is stored at
+ *     chunk position c XOR (((j >> 1) XOR (j >> 2)) AND 3);
+ *   - rows rb*128 + j >= N are zero.
+ * One k-step of a weight tile is then one contiguous stretch of memory that
+ * lands in on-chip memory exactly as the matrix-core reads want it.
+ *
+ * beam_moe_packed_weight_bytes: bytes of one packed N x K expert matrix
+ *   (N, K multiples of 64 in [64, 32768]); 0 if the sizes break that rule.
+ * beam_moe_pack_weights: dst [E * packed bytes] = packed copy of src [E,N,K]
+ *   bf16.  src and dst must not overlap (INVALID_DIM otherwise).  Enqueued on
+ *   `stream`, like every compute call; the caller owns both buffers.
+ */
+size_t beam_moe_packed_weight_bytes(int N, int K);
+int beam_moe_pack_weights(void* stream, int E, int N, int K, const uint16_t* src, uint16_t* dst);
+
+/*
  * Router + group-limited top-k  ([MoE]; router in FP32 per [RES]).
  *   z[t,e]  = sum_h x[t,h] * w_router[e,h]  (+ logit_offset[e])   FP32 accumulate
  *   s[t,e]  = 1 / (1 + exp(-z[t,e]))                               FP32
@@ -107,8 +131,9 @@ int beam_moe_permute(void* stream, int64_t T, int E, int k, const int32_t* topk_
  *     o = w_down[e] . h                                       (FP32 accumulate)
  *   y[t] = bf16( sum_j topk_weights[t,j] * o_j )   FP32 sum in slot order j = 0..k-1
  * topk_weights are used as given (the router's weights already hold the scale).
- * x [T,H] bf16; w_gate, w_up [E,I,H] bf16; w_down [E,H,I] bf16; y [T,H] bf16 out;
- * expert_counts [E] int32 out or NULL.
+ * x [T,H] bf16; w_gate, w_up: the packed I x H matrices of the E experts,
+ * w_down: the packed H x I matrices (see beam_moe_pack_weights); y [T,H] bf16
+ * out; expert_counts [E] int32 out or NULL.
  */
 int beam_moe_forward(void* stream, int64_t T, int H, int I, int E, int k, const uint16_t* x,
                      const int32_t* topk_ids, const float* topk_weights, const uint16_t* w_gate,
@@ -117,7 +142,8 @@ int beam_moe_forward(void* stream, int64_t T, int H, int I, int E, int k, const 
 
 /*
  * Whole block: route -> permute -> gate/up GEMM + SwiGLU -> down GEMM -> combine.
- * Same arguments and meaning as route and forward.  topk_ids / topk_weights /
+ * Same arguments and meaning as route and forward (expert weights packed).
+ * topk_ids / topk_weights /
  * expert_counts are outputs and may each be NULL (then they live in the
  * workspace and are not returned).
  */
@@ -139,7 +165,8 @@ int beam_moe_block(void* stream, int64_t T, int H, int I, int E, int groups, int
  *                   sqrt((step-1)/step)*stream + RMSNorm(float(y)) / sqrt(step),
  *                   y [T,H] bf16; step >= 2.
  * beam_moe_sublayer: one sandwich-normed MoE sublayer at residual step `step`:
- *                   x_in = rmsnorm(stream); y = block(x_in); residual_update(y).
+ *                   x_in = rmsnorm(stream); y = block(x_in); residual_update(y)
+ *                   (expert weights packed, as for block).
  *                   moe_input / moe_output [T,H] bf16 receive x_in and y when
  *                   not NULL; topk_ids / topk_weights / expert_counts as in block.
  */

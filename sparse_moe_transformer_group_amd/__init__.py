@@ -6,8 +6,8 @@ ABI declared in include/beam_moe.h; this package is its ctypes binding.
 Importing it fails if the library has not been built.
 """
 from ._lib import (  # noqa: F401
-    BeamMoeError, StageTimer, block, forward, get_workspace, lib, permute, release_workspaces,
-    residual_update, rmsnorm, route, set_schedule, stage_names, stream_init, sublayer, version,
-    workspace_bytes,
+    BeamMoeError, PackedMatrix, StageTimer, block, forward, get_workspace, lib, pack_experts,
+    pack_weights, packed_weight_bytes, permute, release_workspaces, residual_update, rmsnorm, route,
+    set_schedule, stage_names, stream_init, sublayer, version, workspace_bytes,
 )
 from .build import LIB_PATH  # noqa: F401

@@ -40,6 +40,8 @@ def _load():
         "beam_moe_status_string": (ctypes.c_char_p, [_c_int]),
         "beam_moe_version": (ctypes.c_char_p, []),
         "beam_moe_workspace_bytes": (_c_sz, [_c_i64, _c_int, _c_int, _c_int, _c_int]),
+        "beam_moe_packed_weight_bytes": (_c_sz, [_c_int, _c_int]),
+        "beam_moe_pack_weights": (_c_int, [_c_vp, _c_int, _c_int, _c_int, _c_vp, _c_vp]),
         "beam_moe_route": (_c_int, [_c_vp, _c_i64, _c_int, _c_int, _c_int, _c_int, _c_int, _c_f,
                                     _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_sz]),
         "beam_moe_permute": (_c_int, [_c_vp, _c_i64, _c_int, _c_int, _c_vp, _c_vp, _c_vp, _c_vp,
@@ -183,16 +185,64 @@ def permute(topk_ids, E):
     return counts, offsets, sorted_tokens, row_of
 
 
+class PackedMatrix:
+    """E expert matrices of N x K in the library's packed block layout
+    (see beam_moe_pack_weights in include/beam_moe.h); `data` is the device
+    buffer (uint8)."""
+
+    __slots__ = ("data", "E", "N", "K")
+
+    def __init__(self, data: torch.Tensor, E: int, N: int, K: int):
+        self.data, self.E, self.N, self.K = data, E, N, K
+
+    @property
+    def shape(self):
+        return (self.E, self.N, self.K)
+
+    @property
+    def device(self):
+        return self.data.device
+
+
+def packed_weight_bytes(N: int, K: int) -> int:
+    """Bytes of one packed N x K expert matrix."""
+    n = lib.beam_moe_packed_weight_bytes(int(N), int(K))
+    if n == 0:
+        raise ValueError(f"unsupported matrix shape {N} x {K} (multiples of 64 up to 32768)")
+    return n
+
+
+def pack_weights(w: torch.Tensor) -> PackedMatrix:
+    """Packed copy of expert matrices w [E, N, K] bf16 (nn.Linear layout)."""
+    E, N, K = w.shape
+    _dev_tensor(w, "w", torch.bfloat16, (E, N, K))
+    out = torch.empty((E * packed_weight_bytes(N, K),), dtype=torch.uint8, device=w.device)
+    _check("beam_moe_pack_weights",
+           lib.beam_moe_pack_weights(_stream(w.device), E, N, K, _ptr(w), _ptr(out)))
+    return PackedMatrix(out, E, N, K)
+
+
+def pack_experts(w_gate, w_up, w_down):
+    """(gate, up, down) in the packed layout the compute calls take."""
+    return pack_weights(w_gate), pack_weights(w_up), pack_weights(w_down)
+
+
 def _expert_shapes(w_gate, w_up, w_down):
+    for name, m in (("w_gate", w_gate), ("w_up", w_up), ("w_down", w_down)):
+        if not isinstance(m, PackedMatrix):
+            raise TypeError(f"{name} must be packed with pack_weights / pack_experts")
+        if not m.data.is_cuda:
+            raise ValueError(f"{name} must be a device buffer")
     E, I, H = w_gate.shape
-    _dev_tensor(w_gate, "w_gate", torch.bfloat16, (E, I, H))
-    _dev_tensor(w_up, "w_up", torch.bfloat16, (E, I, H))
-    _dev_tensor(w_down, "w_down", torch.bfloat16, (E, H, I))
+    if w_up.shape != (E, I, H) or w_down.shape != (E, H, I):
+        raise ValueError(f"expert shapes disagree: gate {w_gate.shape}, up {w_up.shape}, "
+                         f"down {w_down.shape}")
     return E, I, H
 
 
 def forward(x, topk_ids, topk_weights, w_gate, w_up, w_down, return_counts=False):
-    """Experts + combine with given routing.  Returns y bf16 [T,H] (and counts)."""
+    """Experts + combine with given routing; expert weights packed (pack_experts).
+    Returns y bf16 [T,H] (and counts)."""
     E, I, H = _expert_shapes(w_gate, w_up, w_down)
     T, k = topk_ids.shape
     dev = x.device
@@ -203,7 +253,7 @@ def forward(x, topk_ids, topk_weights, w_gate, w_up, w_down, return_counts=False
     counts = torch.empty((E,), dtype=torch.int32, device=dev) if return_counts else None
     ws = get_workspace(dev, workspace_bytes(T, H, I, E, k))
     rc = lib.beam_moe_forward(_stream(dev), T, H, I, E, k, _ptr(x), _ptr(topk_ids),
-                              _ptr(topk_weights), _ptr(w_gate), _ptr(w_up), _ptr(w_down), _ptr(y),
+                              _ptr(topk_weights), _ptr(w_gate.data), _ptr(w_up.data), _ptr(w_down.data), _ptr(y),
                               _ptr(counts), _ptr(ws), ws.numel())
     _check("beam_moe_forward", rc)
     return (y, counts) if return_counts else y
@@ -211,7 +261,8 @@ def forward(x, topk_ids, topk_weights, w_gate, w_up, w_down, return_counts=False
 
 def block(x, w_router, w_gate, w_up, w_down, groups=8, topk_groups=4, k=8, scale=2.5,
           logit_offset=None, out=None, return_routing=True):
-    """Whole MoE block.  Returns (y, ids, weights, counts) or y."""
+    """Whole MoE block; expert weights packed (pack_experts).
+    Returns (y, ids, weights, counts) or y."""
     E, I, H = _expert_shapes(w_gate, w_up, w_down)
     T = x.shape[0]
     dev = x.device
@@ -228,8 +279,8 @@ def block(x, w_router, w_gate, w_up, w_down, groups=8, topk_groups=4, k=8, scale
         counts = torch.empty((E,), dtype=torch.int32, device=dev)
     ws = get_workspace(dev, workspace_bytes(T, H, I, E, k))
     rc = lib.beam_moe_block(_stream(dev), T, H, I, E, groups, topk_groups, k, float(scale), _ptr(x),
-                            _ptr(w_router), _ptr(logit_offset), _ptr(w_gate), _ptr(w_up),
-                            _ptr(w_down), _ptr(y), _ptr(ids), _ptr(w), _ptr(counts), _ptr(ws),
+                            _ptr(w_router), _ptr(logit_offset), _ptr(w_gate.data), _ptr(w_up.data),
+                            _ptr(w_down.data), _ptr(y), _ptr(ids), _ptr(w), _ptr(counts), _ptr(ws),
                             ws.numel())
     _check("beam_moe_block", rc)
     return (y, ids, w, counts) if return_routing else y
@@ -279,8 +330,8 @@ def sublayer(stream_io, step, w_router, w_gate, w_up, w_down, groups=8, topk_gro
         counts = torch.empty((E,), dtype=torch.int32, device=dev)
     ws = get_workspace(dev, workspace_bytes(T, H, I, E, k))
     rc = lib.beam_moe_sublayer(_stream(dev), T, H, I, E, groups, topk_groups, k, float(scale),
-                               float(eps), int(step), _ptr(stream_io), _ptr(w_router), _ptr(w_gate),
-                               _ptr(w_up), _ptr(w_down), _ptr(xin), _ptr(yb), _ptr(ids), _ptr(w),
+                               float(eps), int(step), _ptr(stream_io), _ptr(w_router), _ptr(w_gate.data),
+                               _ptr(w_up.data), _ptr(w_down.data), _ptr(xin), _ptr(yb), _ptr(ids), _ptr(w),
                                _ptr(counts), _ptr(ws), ws.numel())
     _check("beam_moe_sublayer", rc)
     return (xin, yb, ids, w, counts) if keep_io else None

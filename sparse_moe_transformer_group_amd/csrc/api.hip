@@ -138,11 +138,13 @@ int device_check(int* num_cu) {
 // ---------------------------------------------------------------- schedule knob
 std::atomic<int> g_schedule{0};  // 0 auto, 1 stream, 2 tiled
 
-// The tiled kernels address one expert's weight matrix and the activation
-// tensor with 32-bit buffer offsets; larger tensors take the streaming path.
+// The tiled kernels address one expert's packed weight matrix and the
+// activation tensor with 32-bit buffer offsets; larger tensors take the
+// streaming path.
 bool tiled_fits(int64_t T, int H, int I, int k) {
   const int64_t lim = int64_t(1) << 31;
-  return (int64_t)H * I * 2 < lim && T * H * 2 < lim && T * k * I * 2 < lim;
+  return packed_expert_bytes(I, H) < lim && packed_expert_bytes(H, I) < lim && T * H * 2 < lim &&
+         T * k * I * 2 < lim;
 }
 
 bool use_stream(int64_t T, int H, int I, int k, int E) {
@@ -272,6 +274,26 @@ const char* beam_moe_status_string(int status) {
 }
 
 const char* beam_moe_version(void) { return "0.1.0"; }
+
+size_t beam_moe_packed_weight_bytes(int N, int K) {
+  if (bad_dim64(N) || bad_dim64(K)) return 0;
+  return (size_t)packed_expert_bytes(N, K);
+}
+
+int beam_moe_pack_weights(void* stream, int E, int N, int K, const uint16_t* src, uint16_t* dst) {
+  if (E < 1 || E > kMaxE || bad_dim64(N) || bad_dim64(K)) return BEAM_MOE_ERR_INVALID_DIM;
+  int rc = check_ptrs({src, dst}, {});
+  if (rc) return rc;
+  // the source and the packed copy must not overlap
+  const char* s0 = reinterpret_cast<const char*>(src);
+  const char* d0 = reinterpret_cast<const char*>(dst);
+  const int64_t sb = (int64_t)E * N * K * 2, db = (int64_t)E * packed_expert_bytes(N, K);
+  if (s0 < d0 + db && d0 < s0 + sb) return BEAM_MOE_ERR_INVALID_DIM;
+  int num_cu;
+  if ((rc = device_check(&num_cu))) return rc;
+  return launch_pack((hipStream_t)stream, src, dst, E, N, K) == hipSuccess ? BEAM_MOE_OK
+                                                                           : BEAM_MOE_ERR_HIP;
+}
 
 size_t beam_moe_workspace_bytes(int64_t T, int H, int I, int E, int k) {
   if (check_forward_dims(T, H, I, E, k) != BEAM_MOE_OK) return 0;

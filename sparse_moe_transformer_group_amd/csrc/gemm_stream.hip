@@ -58,19 +58,28 @@ __global__ __launch_bounds__(256) void grouped_stream_kernel(GroupedArgs a) {
   const int N = a.N, K = a.K;
   unsigned char* tile = lds[wave];
 
-  // Load slot i of this lane: wave row rw = 4i + lane/16, 16-byte chunk lane%16.
-  const uint16_t* lp[LD];
+  // Weights come in the packed block layout: a 128-k step of the wave's
+  // ROWS rows is ROWS/16 row groups x 4 k-blocks, each 16 rows x 64 bytes
+  // contiguous (1 KB, one wave load).  Load i covers row group i/4 and
+  // k-block i%4; lane l takes row l/4 of the group and physical chunk l%4,
+  // i.e. logical chunk (l%4) ^ swz(row).  f0 is a multiple of 16, so the
+  // row groups never cross a 128-row block.
+  const int64_t ebytes = packed_expert_bytes(N, K);
+  const int nkb = K / kPackK;
+  const int rb = f0 / kPackRows, rib0 = f0 % kPackRows;
+  const unsigned char* lp[LD];
   int lo[LD];
 #pragma unroll
   for (int i = 0; i < LD; ++i) {
-    const int rw = 4 * i + (lane >> 4);
-    const int c = lane & 15;
-    const int m = rw / (RB * 16);
-    const int fr = rw % (RB * 16);
-    const int f = min(f0 + fr, N - 1);
-    const uint16_t* base = (m == 0) ? a.w0 : a.w1;
-    lp[i] = base + ((int64_t)e * N + f) * K + c * 8;
-    lo[i] = rw * 256 + ((c ^ (rw & 15)) << 4);
+    const int grp = i >> 2, kbl = i & 3;
+    const int j = lane >> 2, pc = lane & 3;
+    const int c = pc ^ pack_swz(j);
+    const int m = (grp * 16) / (RB * 16);           // matrix (gate / up) of this row group
+    const int rib = rib0 + (grp * 16) % (RB * 16) + j;  // row inside the 128-row block
+    const unsigned char* base = reinterpret_cast<const unsigned char*>(m == 0 ? a.w0 : a.w1);
+    lp[i] = base + e * ebytes + ((int64_t)(rb * nkb + kbl) * kPackRows + rib) * 64 + pc * 16;
+    const int rw = grp * 16 + j;                      // row of the wave's LDS tile
+    lo[i] = rw * 256 + (((4 * kbl + c) ^ (rw & 15)) << 4);
   }
 
   for (int c0 = 0; c0 < n_e; c0 += 16 * MT) {
@@ -97,7 +106,7 @@ __global__ __launch_bounds__(256) void grouped_stream_kernel(GroupedArgs a) {
     uint4 B[2][MT][4];
     auto load_w = [&](int ks) {
 #pragma unroll
-      for (int i = 0; i < LD; ++i) R[i] = ld16_nt(lp[i] + ks * 128);
+      for (int i = 0; i < LD; ++i) R[i] = ld16_nt(lp[i] + (int64_t)ks * 4 * kPackBlockBytes);
     };
     auto load_b = [&](int buf, int ks) {
 #pragma unroll
@@ -155,9 +164,12 @@ __global__ __launch_bounds__(256) void grouped_stream_kernel(GroupedArgs a) {
         for (int m = 0; m < MAT; ++m)
 #pragma unroll
           for (int i = 0; i < RB; ++i) {
-            const int f = min(f0 + 16 * i + r, N - 1);
-            const uint16_t* base = (m == 0) ? a.w0 : a.w1;
-            const uint4 at = ld16(base + ((int64_t)e * N + f) * K + kt + q * 16 + c * 8);
+            // k = kt + 16q + 8c: k-block kt/32 + q/2, logical chunk 2(q%2) + c
+            const int rib = rib0 + 16 * i + r;
+            const int kb = kt / kPackK + (q >> 1);
+            const int pc = (2 * (q & 1) + c) ^ pack_swz(r);
+            const unsigned char* base = reinterpret_cast<const unsigned char*>(m == 0 ? a.w0 : a.w1);
+            const uint4 at = ld16(base + e * ebytes + ((int64_t)(rb * nkb + kb) * kPackRows + rib) * 64 + pc * 16);
 #pragma unroll
             for (int t = 0; t < MT; ++t) acc[m][i][t] = mfma16(at, bt[t], acc[m][i][t]);
           }

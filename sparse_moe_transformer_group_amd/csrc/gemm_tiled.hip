@@ -38,6 +38,7 @@ __device__ __forceinline__ f32x16 mfma32(uint4 a, uint4 b, f32x16 c) {
 constexpr int kMaxE = 512;
 constexpr int kBW = 256;                 // weight rows per tile (8 MFMA row blocks of 32)
 constexpr int kBK = 32;                  // k per pipeline step (64 bytes per row)
+static_assert(kBK == kPackK && kBW == 2 * kPackRows, "a k-step is one packed k-block");
 constexpr int kWBytes = kBW * kBK * 2;   // weight slab per step (16 KB)
 
 typedef __attribute__((address_space(3))) void lds_void;
@@ -52,7 +53,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base, uin
 // Physical 16-byte chunk of logical chunk c (0..3) in 64-byte row `row`:
 // XOR by ((row >> 1) ^ (row >> 2)) & 3 keeps the 8-lane and the 16-lane
 // groups of ds_read_b128 conflict-free (32 or 64 banks).
-__device__ __forceinline__ int rchunk(int row, int c) { return c ^ (((row >> 1) ^ (row >> 2)) & 3); }
+__device__ __forceinline__ int rchunk(int row, int c) { return c ^ pack_swz(row); }
 
 // One direct-to-LDS 16-byte-per-lane buffer load: lane l's 16 bytes at
 // rsrc + voff + soff land at LDS byte lds + 16 l.  Issued from inline asm so
@@ -81,38 +82,37 @@ __device__ __forceinline__ void dma16(uint32_t lds, uint32_t voff, __amdgpu_buff
     __builtin_amdgcn_sched_barrier(0);                                          \
   } while (0)
 
-// Workgroup tile: 256 weight rows x BM tokens, 4 waves; wave w owns tokens
-// [w*BM/4, (w+1)*BM/4) of the tile (NB = BM/128 MFMA column blocks of 32)
-// and all 256 weight rows (8 MFMA row blocks):
-// gate/up (MAT = 2): blocks 0-3 = gate rows of features [f, f+128) and
-// blocks 4-7 = the up rows of the same features, so SiLU(g)*u pairs sit in
-// one lane; down (MAT = 1): 256 features.  Accumulators: 8 x NB 32x32 blocks.
+// Workgroup tile: 256 weight rows x up to 256 tokens of one expert, 4 waves.
+// Wave w owns 64 weight rows and every token of the tile, so the MFMA work
+// of a tile is proportional to its token blocks (32 tokens each) and equal on
+// the 4 SIMDs:
+//   gate/up (MAT = 2): wave w holds the gate rows (block 0) and the up rows
+//     (block 1) of features [f0 + 32w, f0 + 32w + 32), so SiLU(g)*u pairs sit
+//     in one lane; a tile covers 128 features;
+//   down (MAT = 1): rows [f0 + 64w, f0 + 64w + 64); a tile covers 256.
+// Accumulators: 2 x NB blocks of 32x32 FP32 (NB = token blocks, 1..8).
 //
 // At prefill sizes an expert's weights feed only ~256 tokens, about 256
 // FLOP per weight byte -- below MI355X's MFMA/HBM ridge -- so the tile is
-// built to keep HBM busy.  Each k-step (32 wide) moves a 16 KB weight slab
-// and each wave's BM/4 x 64-byte token slab straight into an LDS ring of
+// built to keep HBM busy.  Each k-step (32 wide) moves the 16 KB weight slab
+// and the tile's token slab (64 bytes per token) straight into an LDS ring of
 // STAGES stages with direct-to-LDS buffer loads -- no vector registers are
-// spent on staging.  A wave instruction fills 16 rows x 64 bytes; lane l
-// takes the 16-byte chunk that lands in physical slot l%4 of its row.  One
-// wait + barrier per step publishes a stage and frees the one read a step
-// earlier.  With PAIR = 2 loads go out two steps at a time, so each weight
-// row sees back-to-back requests for 128 contiguous bytes.  Token blocks
-// past the tile's last token skip their loads and MFMAs: the k-loop is
-// specialised on the number of valid blocks (wave-uniform).  With OCC = 2
-// two workgroups share a CU, so one's waits overlap the other's MFMAs.
+// spent on staging.  A load instruction fills 16 rows x 64 bytes; lane l
+// takes the 16-byte chunk that lands in physical slot l%4 of its row.  The
+// loads of a step go out one instruction every few MFMAs of an earlier step
+// (a full address queue then stalls a wave only briefly while its MFMAs keep
+// the pipe busy).  One wait + barrier per step publishes a stage and frees
+// the one read a step earlier.
 //
 // MFMA s (0..1) of a step uses 16-byte chunk 2s+g of each row for lane group
 // g = l/32 of both operands.
-template <int MAT, int BM, int STAGES, int PAIR, int OCC>
+template <int MAT, int BM, int STAGES, int OCC>
 __global__ __launch_bounds__(256, OCC) void grouped_tiled_kernel(GroupedArgs a) {
-  static_assert(BM == 128 || BM == 256, "4 waves x 32 or 64 tokens");
-  static_assert(PAIR == 1 || (PAIR == 2 && STAGES == 4), "paired issue needs 4 stages");
-  static_assert(STAGES >= 2 && STAGES * (kWBytes + BM * kBK * 2) <= 160 * 1024 - 4096, "LDS");
-  constexpr int NB = BM / 128;                 // 32-token MFMA blocks per wave
+  static_assert(BM == 128 || BM == 256, "tokens per tile");
   constexpr int TBytes = BM * kBK * 2;         // token slab per step
   constexpr int Stage = kWBytes + TBytes;
   constexpr int F = (MAT == 2) ? kBW / 2 : kBW;  // output features per tile
+  static_assert(STAGES >= 3 && STAGES * Stage <= 160 * 1024 / OCC - 4096, "LDS");
   __shared__ __attribute__((aligned(1024))) unsigned char ring[STAGES * Stage];
   __shared__ int s_start[kMaxE + 1];
   __shared__ int s_scan[256];
@@ -149,15 +149,17 @@ __global__ __launch_bounds__(256, OCC) void grouped_tiled_kernel(GroupedArgs a) 
   const int span = (total + 7) / 8;
   const int lo = xcd * span, hi = min(total, lo + span);
   const int nk = K / kBK;
-  const uint32_t wbytes = (uint32_t)N * (uint32_t)K * 2u;  // one expert matrix (< 2^31)
+  const uint32_t wbytes = (uint32_t)packed_expert_bytes(N, K);  // one packed expert matrix (< 2^31)
   const __amdgpu_buffer_rsrc_t rs_act = buf_rsrc(a.act, 0x7fffffffu);
   const uint32_t ring_lds = (uint32_t)(uintptr_t)(lds_void*)ring;
 
-  // Per-lane byte offsets inside a stage (same for every stage).
+  // Per-lane byte offsets inside a stage (same for every stage).  The chunk
+  // swizzle depends on the row's low bits only, so it is the same for row r
+  // of every 32-row block.
   const int lrow = lane >> 2, lpc = lane & 3;  // DMA: row within a 16-row group, physical chunk
-  const uint32_t a_rd = r * 64 + (rchunk(r, g) << 4);          // weight operand, s = 0, block 0
-  const uint32_t a_rd1 = r * 64 + (rchunk(r, 2 + g) << 4);     // s = 1
-  const uint32_t t_rd = kWBytes + wave * (TBytes / 4);         // this wave's token region
+  const uint32_t c_rd0 = r * 64 + (rchunk(r, g) << 4);      // MFMA s = 0, row r of a block
+  const uint32_t c_rd1 = r * 64 + (rchunk(r, 2 + g) << 4);  // MFMA s = 1
+  const uint32_t w_base = wave * (kWBytes / 4);              // this wave's 64 weight rows
 
   for (int tile = lo + slot; tile < hi; tile += per_xcd) {
     // expert: largest e with s_start[e] <= tile
@@ -180,185 +182,155 @@ __global__ __launch_bounds__(256, OCC) void grouped_tiled_kernel(GroupedArgs a) 
     // most BM): sibling tiles of one weight tile then do equal work, run side
     // by side on one XCD (adjacent tile ids) and share the weight stream
     // through L2 instead of each reading it from HBM.
-    const int m0 = (int)((int64_t)mtile * n_e / mt_e);
-    const int m1 = (int)((int64_t)(mtile + 1) * n_e / mt_e);
-    const int tw0 = __builtin_amdgcn_readfirstlane(m0 + wave * (BM / 4));  // this wave's first token
-    const int nbv = max(0, min(NB, (m1 - tw0 + 31) / 32));             // its blocks holding a token
+    const int m0 = __builtin_amdgcn_readfirstlane((int)((int64_t)mtile * n_e / mt_e));
+    const int m1 = __builtin_amdgcn_readfirstlane((int)((int64_t)(mtile + 1) * n_e / mt_e));
+    const int nb = (m1 - m0 + 31) / 32;  // token blocks of the tile, 1..BM/32
 
-    // Weight DMA: wave instruction i (0..3) fills tile rows 64w + 16i .. +16.
-    // Rows 0..127 of a gate/up tile are gate rows (waves 0, 1), 128..255 up rows.
-    const __amdgpu_buffer_rsrc_t rs_w =
-        buf_rsrc(((MAT == 2 && wave >= 2) ? a.w1 : a.w0) + (int64_t)e * N * K, wbytes);
+    // Weight DMA from the packed layout: instruction i (0..3) copies 16 rows
+    // x 64 bytes (1 KB, contiguous) of this wave's 128-row block into its
+    // rows 16i .. 16i+15; the packed chunk order is already the LDS order.
+    // Gate/up: rows 0..31 are gate rows, 32..63 the up rows of the same
+    // features (block ftile, rows 32w ..); down: block 2*ftile + w/2, rows
+    // 64*(w%2) ...  A block past the matrix (odd block count, down) reads
+    // as zeros through the buffer bounds.
+    const int fw = (MAT == 2) ? fbase + 32 * wave : fbase + 64 * wave;  // this wave's first feature
+    const char* wexp0 = reinterpret_cast<const char*>(a.w0) + (int64_t)e * wbytes;
+    const char* wexp1 = reinterpret_cast<const char*>(MAT == 2 ? a.w1 : a.w0) + (int64_t)e * wbytes;
+    const __amdgpu_buffer_rsrc_t rs_w0 = buf_rsrc(wexp0, wbytes);
+    const __amdgpu_buffer_rsrc_t rs_w1 = buf_rsrc(wexp1, wbytes);
     uint32_t woff[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int row = 64 * wave + 16 * i + lrow;
-      const int f = (MAT == 2) ? fbase + (row % F) : fbase + row;
-      woff[i] = ((uint32_t)min(f, N - 1) * (uint32_t)K) * 2u + (rchunk(row, lpc) << 4);
-    }
-    // Token DMA: wave instruction i fills this wave's token rows 16i .. +16.
-    uint32_t toff[2 * NB];
-#pragma unroll
-    for (int i = 0; i < 2 * NB; ++i) {
-      const int trow = 16 * i + lrow;
-      const int tok = max(0, min(tw0 + trow, m1 - 1));
-      const int rr = row0 + tok;
-      const uint32_t src = a.sorted_tokens ? (uint32_t)a.sorted_tokens[rr] : (uint32_t)rr;
-      toff[i] = src * (uint32_t)K * 2u + (rchunk(trow, lpc) << 4);
+      const int blk = (MAT == 2) ? ftile : 2 * ftile + (wave >> 1);
+      const int brow = (MAT == 2) ? 32 * wave + 16 * (i & 1) : 64 * (wave & 1) + 16 * i;
+      woff[i] = ((uint32_t)blk * (uint32_t)nk * kPackRows + (uint32_t)brow) * 64u + lane * 16u;
     }
 
-    // k-loop and epilogue, specialised on the number of valid token blocks
-    auto run = [&](auto NBVc) {
-      constexpr int NBV = decltype(NBVc)::value;
-      constexpr int LPS = 4 + 2 * NBV;  // direct-to-LDS loads per step and wave
-      f32x16 acc[8][NB];
+    // k-loop and epilogue, specialised on the number of token blocks
+    auto run = [&](auto NBc) {
+      constexpr int NB = decltype(NBc)::value;
+      // Token DMA: 2*NB instructions of 16 rows, instruction 4q + w issued
+      // by wave w; every wave issues TPW of them (rows past the tile's last
+      // token load that token again and are never read).
+      constexpr int TPW = (2 * NB + 3) / 4;
+      constexpr int LPS = 4 + TPW;  // direct-to-LDS loads per step and wave
+      uint32_t toff[TPW];
 #pragma unroll
-      for (int b = 0; b < 8; ++b)
+      for (int q = 0; q < TPW; ++q) {
+        const int trow = 16 * (4 * q + wave) + lrow;
+        const int tok = min(m0 + trow, m1 - 1);
+        const int rr = row0 + tok;
+        const uint32_t src = a.sorted_tokens ? (uint32_t)a.sorted_tokens[rr] : (uint32_t)rr;
+        toff[q] = src * (uint32_t)K * 2u + (rchunk(trow, lpc) << 4);
+      }
+
+      f32x16 acc[2][NB];
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
 #pragma unroll
         for (int j = 0; j < NB; ++j)
 #pragma unroll
           for (int i = 0; i < 16; ++i) acc[b][j][i] = 0.f;
 
+      auto dma_op = [&](int d, uint32_t st, uint32_t so) {
+        if (d < 4)  // weights: k-block kt of the packed block, so * 128 = kt * 8 KB
+          dma16(__builtin_amdgcn_readfirstlane(st + w_base + 16 * d * 64), woff[d],
+                (MAT == 2 && d >= 2) ? rs_w1 : rs_w0, so * (kPackBlockBytes / (kBK * 2)));
+        else
+          dma16(__builtin_amdgcn_readfirstlane(st + kWBytes + 16 * (4 * (d - 4) + wave) * 64),
+                toff[d - 4], rs_act, so);
+      };
       auto issue = [&](int kt) {  // loads of step kt into stage kt % STAGES
         const uint32_t st = ring_lds + (kt % STAGES) * Stage;
         const uint32_t so = (uint32_t)kt * (kBK * 2);
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          dma16(__builtin_amdgcn_readfirstlane(st + (64 * wave + 16 * i) * 64), woff[i], rs_w, so);
-#pragma unroll
-        for (int i = 0; i < 2 * NBV; ++i)
-          dma16(__builtin_amdgcn_readfirstlane(st + t_rd + 16 * i * 64), toff[i], rs_act, so);
+        for (int d = 0; d < LPS; ++d) dma_op(d, st, so);
       };
 
       // Step s may load into the stage of step s-1 (fully read before the
-      // barrier of step s-1), so loads run up to STAGES-1 steps ahead.  Issue
-      // points are the steps s with s % PAIR == 0; each issues steps
-      // s+STAGES-PAIR .. s+STAGES-1 (clamped to the last step, so every issue
-      // point issues PAIR steps and the wait counts below stay exact).  Step
-      // s+1 must have landed at the barrier of step s; the steps issued after
-      // it are still allowed in flight: STAGES-2-(s % PAIR) of them.
-      // Prologue: steps 0 .. STAGES-PAIR-1, step 0 published.
+      // barrier of step s-1), so loads run STAGES-1 steps ahead.  Step
+      // min(s+STAGES-1, nk-1) goes out during step s: past the last step the
+      // clamp re-loads step nk-1 into its own stage (identical bytes, so its
+      // readers see the same values), and every step issues LPS loads, which
+      // keeps the wait counts exact.  Step s+1 must have landed at the
+      // barrier of step s; the STAGES-2 steps issued after it may still be in
+      // flight.  Prologue: steps 0 .. STAGES-2, step 0 published.
 #pragma unroll
-      for (int q = 0; q < STAGES - PAIR; ++q) issue(min(q, nk - 1));
-      BEAM_STEP_BARRIER((STAGES - PAIR - 1) * LPS);
+      for (int q = 0; q < STAGES - 1; ++q) issue(min(q, nk - 1));
+      BEAM_STEP_BARRIER((STAGES - 2) * LPS);
 
       // Operands of MFMA s of the step whose stage starts at sb.
-      auto read_ops = [&](const unsigned char* sb, int s, uint4 (&af)[8], uint4 (&bf)[NB]) {
-        const unsigned char* wa = sb + (s ? a_rd1 : a_rd);
+      auto read_ops = [&](const unsigned char* sb, int s, uint4 (&af)[2], uint4 (&bf)[NB]) {
+        const uint32_t c = s ? c_rd1 : c_rd0;
 #pragma unroll
-        for (int b = 0; b < 8; ++b) af[b] = *reinterpret_cast<const uint4*>(wa + 2048 * b);
+        for (int b = 0; b < 2; ++b)
+          af[b] = *reinterpret_cast<const uint4*>(sb + w_base + 2048 * b + c);
 #pragma unroll
-        for (int j = 0; j < NBV; ++j) bf[j] = *reinterpret_cast<const uint4*>(wa + t_rd + 2048 * j);
+        for (int j = 0; j < NB; ++j)
+          bf[j] = *reinterpret_cast<const uint4*>(sb + kWBytes + 2048 * j + c);
         __builtin_amdgcn_sched_barrier(0);  // reads go out before the MFMAs that follow
-      };
-      auto mfmas = [&](const uint4 (&af)[8], const uint4 (&bf)[NB]) {
-#pragma unroll
-        for (int j = 0; j < NBV; ++j)
-#pragma unroll
-          for (int b = 0; b < 8; ++b) acc[b][j] = mfma32(af[b], bf[j], acc[b][j]);
       };
 
       // Software pipeline: the barrier publishing step kt+1 sits between
       // the two MFMA groups of step kt, so the reads of the next group are
       // always in flight while the current one runs.
-      uint4 af0[8], bf0[NB], af1[8], bf1[NB];
-      if constexpr (NBV > 0) read_ops(ring, 0, af0, bf0);
-      auto kstep = [&](auto PHASE, int kt) {
-        constexpr int ph = decltype(PHASE)::value;  // kt % PAIR
+      uint4 af0[2], bf0[NB], af1[2], bf1[NB];
+      read_ops(ring, 0, af0, bf0);
+      for (int kt = 0; kt < nk; ++kt) {
         const unsigned char* sb = ring + (kt % STAGES) * Stage;
-        if constexpr (PAIR == 1) {
-          // Single issue, spread over the MFMAs: step min(kt+STAGES-1, nk-1)
-          // goes out one instruction every few MFMAs, so a full address queue
-          // stalls this wave only briefly while its MFMAs keep the pipe busy.
-          // Past the last step the clamp re-loads step nk-1 into its own
-          // stage: identical bytes, so the readers of that stage see the same
-          // values, and every step issues LPS loads (exact wait counts).
-          const int ki = min(kt + STAGES - 1, nk - 1);
-          const uint32_t st = ring_lds + (ki % STAGES) * Stage;
-          const uint32_t so = (uint32_t)ki * (kBK * 2);
-          auto dma_op = [&](int d) {
-            if (d < 4) dma16(__builtin_amdgcn_readfirstlane(st + (64 * wave + 16 * d) * 64), woff[d], rs_w, so);
-            else dma16(__builtin_amdgcn_readfirstlane(st + t_rd + 16 * (d - 4) * 64), toff[d - 4], rs_act, so);
-          };
-          if constexpr (NBV > 0) {
-            read_ops(sb, 1, af1, bf1);
-            constexpr int NM = 8 * NBV;
-            constexpr int EVERY = NM / LPS > 0 ? NM / LPS : 1;
-            int d = 0;
+        const int ki = min(kt + STAGES - 1, nk - 1);
+        const uint32_t st = ring_lds + (ki % STAGES) * Stage;
+        const uint32_t so = (uint32_t)ki * (kBK * 2);
+        read_ops(sb, 1, af1, bf1);
+        {
+          constexpr int NM = 2 * NB;
+          constexpr int EVERY = NM / LPS > 0 ? NM / LPS : 1;
+          int d = 0;
 #pragma unroll
-            for (int m = 0; m < NM; ++m) {
-              acc[m % 8][m / 8] = mfma32(af0[m % 8], bf0[m / 8], acc[m % 8][m / 8]);
-              if (m % EVERY == EVERY - 1 && d < LPS) {
-                dma_op(d);
-                ++d;
-                __builtin_amdgcn_sched_barrier(0);
-              }
+          for (int m = 0; m < NM; ++m) {
+            acc[m & 1][m >> 1] = mfma32(af0[m & 1], bf0[m >> 1], acc[m & 1][m >> 1]);
+            if (m % EVERY == EVERY - 1 && d < LPS) {
+              dma_op(d, st, so);
+              ++d;
+              __builtin_amdgcn_sched_barrier(0);
             }
-#pragma unroll
-            for (; d < LPS; ++d) dma_op(d);
-          } else {
-#pragma unroll
-            for (int d = 0; d < LPS; ++d) dma_op(d);
           }
-          // this wave's loads of step kt+1 have landed and its reads of stage
-          // kt are done; after the barrier, the same holds for every wave
-          BEAM_STEP_BARRIER((STAGES - 2) * LPS);
-        } else {
-          const bool issued = kt - ph + STAGES - PAIR < nk;  // this step's issue point issued
-          if (ph == 0 && issued) {
 #pragma unroll
-            for (int q = STAGES - PAIR; q < STAGES; ++q) issue(min(kt + q, nk - 1));
-          }
-          if constexpr (NBV > 0) {
-            read_ops(sb, 1, af1, bf1);
-            mfmas(af0, bf0);
-          }
-          if (issued) BEAM_STEP_BARRIER((STAGES - 2 - ph) * LPS);
-          else BEAM_STEP_BARRIER(0);
+          for (; d < LPS; ++d) dma_op(d, st, so);
         }
-        if constexpr (NBV > 0) {
-          // next step's first operands (after the last step: a stale stage, unused)
-          read_ops(ring + ((kt + 1) % STAGES) * Stage, 0, af0, bf0);
-          mfmas(af1, bf1);
-        }
-      };
-      int kt = 0;
-      if constexpr (PAIR == 2) {
-        for (; kt + 2 <= nk; kt += 2) {
-          kstep(std::integral_constant<int, 0>{}, kt);
-          kstep(std::integral_constant<int, 1>{}, kt + 1);
-        }
-        if (kt < nk) kstep(std::integral_constant<int, 0>{}, kt);
-      } else {
-        for (; kt < nk; ++kt) kstep(std::integral_constant<int, 0>{}, kt);
+        // this wave's loads of step kt+1 have landed and its reads of stage
+        // kt are done; after the barrier, the same holds for every wave
+        BEAM_STEP_BARRIER((STAGES - 2) * LPS);
+        // next step's first operands (after the last step: a stale stage, unused)
+        read_ops(ring + ((kt + 1) % STAGES) * Stage, 0, af0, bf0);
+#pragma unroll
+        for (int m = 0; m < 2 * NB; ++m)
+          acc[m & 1][m >> 1] = mfma32(af1[m & 1], bf1[m >> 1], acc[m & 1][m >> 1]);
       }
       BEAM_STEP_BARRIER(0);  // drain the clamped prefetches; the next tile may refill the ring
 
-      // Epilogue: acc[b][j][i] is row 8*(i/4) + 4*g + (i%4) of weight block
-      // b, token tw0 + 32*j + r.
+      // Epilogue: acc[b][j][i] is row 8*(i/4) + 4*g + (i%4) of this wave's
+      // weight block b, token m0 + 32*j + r.
 #pragma unroll
-      for (int j = 0; j < NBV; ++j) {
-        const int tok = tw0 + 32 * j + r;
+      for (int j = 0; j < NB; ++j) {
+        const int tok = m0 + 32 * j + r;
         if (tok >= m1) continue;
         const int64_t row = row0 + tok;
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) {
           if constexpr (MAT == 2) {
+            const int f = fw + 8 * q4 + 4 * g;
+            if (f >= N) continue;
+            uint32_t p[4];
 #pragma unroll
-            for (int b = 0; b < 4; ++b) {
-              const int f = fbase + 32 * b + 8 * q4 + 4 * g;
-              if (f >= N) continue;
-              uint32_t p[4];
-#pragma unroll
-              for (int c = 0; c < 4; ++c)
-                p[c] = f32_to_bf16_rne(swiglu(acc[b][j][4 * q4 + c], acc[b + 4][j][4 * q4 + c]));
-              *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + row * N + f) =
-                  make_uint2(p[0] | (p[1] << 16), p[2] | (p[3] << 16));
-            }
+            for (int c = 0; c < 4; ++c)
+              p[c] = f32_to_bf16_rne(swiglu(acc[0][j][4 * q4 + c], acc[1][j][4 * q4 + c]));
+            *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + row * N + f) =
+                make_uint2(p[0] | (p[1] << 16), p[2] | (p[3] << 16));
           } else {
 #pragma unroll
-            for (int b = 0; b < 8; ++b) {
-              const int f = fbase + 32 * b + 8 * q4 + 4 * g;
+            for (int b = 0; b < 2; ++b) {
+              const int f = fw + 32 * b + 8 * q4 + 4 * g;
               if (f >= N) continue;
               *reinterpret_cast<f32x4*>(static_cast<float*>(a.out) + row * N + f) =
                   f32x4{acc[b][j][4 * q4], acc[b][j][4 * q4 + 1], acc[b][j][4 * q4 + 2],
@@ -368,36 +340,51 @@ __global__ __launch_bounds__(256, OCC) void grouped_tiled_kernel(GroupedArgs a) 
         }
       }
     };  // run
-    if constexpr (NB == 2) {
-      if (nbv == 2) run(std::integral_constant<int, 2>{});
-      else if (nbv == 1) run(std::integral_constant<int, 1>{});
-      else run(std::integral_constant<int, 0>{});
+    if constexpr (BM == 256) {
+      switch (nb) {
+        case 1: run(std::integral_constant<int, 1>{}); break;
+        case 2: run(std::integral_constant<int, 2>{}); break;
+        case 3: run(std::integral_constant<int, 3>{}); break;
+        case 4: run(std::integral_constant<int, 4>{}); break;
+        case 5: run(std::integral_constant<int, 5>{}); break;
+        case 6: run(std::integral_constant<int, 6>{}); break;
+        case 7: run(std::integral_constant<int, 7>{}); break;
+        default: run(std::integral_constant<int, 8>{}); break;
+      }
     } else {
-      if (nbv == 1) run(std::integral_constant<int, 1>{});
-      else run(std::integral_constant<int, 0>{});
+      switch (nb) {
+        case 1: run(std::integral_constant<int, 1>{}); break;
+        case 2: run(std::integral_constant<int, 2>{}); break;
+        case 3: run(std::integral_constant<int, 3>{}); break;
+        default: run(std::integral_constant<int, 4>{}); break;
+      }
     }
   }
 }
 
-// Tile configuration: BM tokens per tile, ring depth, issue pairing,
-// workgroups per CU.
+// Tile configuration: tokens per tile, ring depth, workgroups per CU.
 #ifndef BEAM_TILED_CFG
-#define BEAM_TILED_CFG 256, 4, 1, 1
+#define BEAM_TILED_CFG 256, 4, 1
 #endif
 
-template <int MAT, int BM, int STAGES, int PAIR, int OCC>
+template <int MAT, int BM, int STAGES, int OCC>
 static hipError_t launch_tiled_cfg(hipStream_t st, const GroupedArgs& a, int num_cu) {
   const int nwg = ((num_cu * OCC + 7) / 8) * 8;  // persistent grid, a multiple of the 8 XCDs
-  hipLaunchKernelGGL((grouped_tiled_kernel<MAT, BM, STAGES, PAIR, OCC>), dim3(nwg), dim3(256), 0, st, a);
+  hipLaunchKernelGGL((grouped_tiled_kernel<MAT, BM, STAGES, OCC>), dim3(nwg), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
+template <int MAT>
+static hipError_t launch_tiled(hipStream_t st, const GroupedArgs& a, int num_cu) {
+  return launch_tiled_cfg<MAT, BEAM_TILED_CFG>(st, a, num_cu);
+}
+
 hipError_t launch_gateup_tiled(hipStream_t st, const GroupedArgs& a, int num_cu) {
-  return launch_tiled_cfg<2, BEAM_TILED_CFG>(st, a, num_cu);
+  return launch_tiled<2>(st, a, num_cu);
 }
 
 hipError_t launch_down_tiled(hipStream_t st, const GroupedArgs& a, int num_cu) {
-  return launch_tiled_cfg<1, BEAM_TILED_CFG>(st, a, num_cu);
+  return launch_tiled<1>(st, a, num_cu);
 }
 
 }  // namespace beam

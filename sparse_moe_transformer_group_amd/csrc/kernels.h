@@ -26,12 +26,29 @@ hipError_t launch_permute(hipStream_t s, const int32_t* ids, int64_t Tk, int k, 
                           int32_t* offsets, int32_t* sorted_tokens, int32_t* row_of,
                           int32_t* user_counts);
 
+// ---- packed expert weights (pack.hip) ----
+// An expert matrix W[N][K] (bf16, K contiguous) is stored as ceil(N/128) row
+// blocks x K/32 k-blocks of 128 rows x 32 k (8 KB each); block (rb, kb) sits
+// at byte (rb * K/32 + kb) * 8192 of the expert, experts back to back.  Row j
+// of a block takes 64 bytes at j * 64; its logical 16-byte chunk c (k = 32 kb
+// + 8c .. 32 kb + 8c + 7) is stored at physical chunk c ^ pack_swz(j).  Rows
+// past N are zero.  A k-step of a tile is then one contiguous stretch of
+// memory, already in the LDS layout the MFMA reads conflict-free.
+constexpr int kPackRows = 128;
+constexpr int kPackK = 32;
+constexpr int kPackBlockBytes = kPackRows * kPackK * 2;
+__host__ __device__ inline int pack_swz(int row) { return ((row >> 1) ^ (row >> 2)) & 3; }
+__host__ __device__ inline int64_t packed_expert_bytes(int N, int K) {
+  return (int64_t)((N + kPackRows - 1) / kPackRows) * (K / kPackK) * kPackBlockBytes;
+}
+hipError_t launch_pack(hipStream_t s, const uint16_t* src, uint16_t* dst, int E, int N, int K);
+
 // ---- grouped expert GEMMs (gemm_stream.hip, gemm_tiled.hip) ----
 struct GroupedArgs {
   const uint16_t* act;          // activations: x [T,H] (gate/up) or h [Tk,I] (down)
   const int32_t* sorted_tokens; // row indirection for x (gate/up); NULL for h
-  const uint16_t* w0;           // gate [E,I,H] or down [E,H,I]
-  const uint16_t* w1;           // up [E,I,H] or NULL
+  const uint16_t* w0;           // packed gate [E,I,H] or down [E,H,I]
+  const uint16_t* w1;           // packed up [E,I,H] or NULL
   const int32_t* counts;        // [E]
   const int32_t* offsets;       // [E+1]
   void* out;                    // h [Tk,I] bf16 or o [Tk,H] fp32

@@ -117,6 +117,21 @@ def test_block_validation():
     assert block(T=0, wsb=need) == 0
 
 
+def test_pack_validation_and_sizes():
+    # one packed expert matrix: ceil(N/128) row blocks x K/32 k-blocks of 8 KB
+    assert lib.beam_moe_packed_weight_bytes(2560, 5120) == 20 * 160 * 8192
+    assert lib.beam_moe_packed_weight_bytes(5120, 2560) == 40 * 80 * 8192
+    assert lib.beam_moe_packed_weight_bytes(192, 64) == 2 * 2 * 8192      # padded to 256 rows
+    assert lib.beam_moe_packed_weight_bytes(100, 64) == 0
+    assert lib.beam_moe_packed_weight_bytes(128, 0) == 0
+    big = 1 << 36
+    assert lib.beam_moe_pack_weights(None, 0, 128, 128, P, big) == -1       # E < 1
+    assert lib.beam_moe_pack_weights(None, 4, 96, 128, P, big) == -1       # N not a multiple of 64
+    assert lib.beam_moe_pack_weights(None, 4, 128, 128, None, big) == -2
+    assert lib.beam_moe_pack_weights(None, 4, 128, 128, P + 8, big) == -3
+    assert lib.beam_moe_pack_weights(None, 4, 128, 128, P, P + 4096) == -1  # overlapping buffers
+
+
 def test_permute_and_helpers_validation():
     assert lib.beam_moe_permute(None, 10, 0, 8, P, P, P, P, P, P, BIG) == -1
     assert lib.beam_moe_permute(None, 10, 256, 8, P, P, None, P, P, P, BIG) == -2

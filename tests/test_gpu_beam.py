@@ -37,24 +37,25 @@ def bm():
 
 
 @pytest.fixture(scope="module")
-def beam_weights():
+def beam_weights(bm):
     s = MI.WORKLOADS["prefill"]
     print("[setup] Beam-shape weights layer 0", flush=True)
     wr = MI.make_router(s.E, s.H).to(DEV)
     wg, wu, wd = MI.make_expert_weights(s.E, s.H, s.I, DEV)
+    packed = bm.pack_experts(wg, wu, wd)
     sync()
-    yield wr, wg, wu, wd
-    del wg, wu, wd
+    yield wr, wg, wu, wd, packed
+    del wg, wu, wd, packed
     torch.cuda.empty_cache()
 
 
 def beam_case(bm, beam_weights, name):
     shape = MI.WORKLOADS[name]
     print(f"[case] {name} T={shape.T}", flush=True)
-    wr, wg, wu, wd = beam_weights
+    wr, wg, wu, wd, packed = beam_weights
     x = MI.make_x(shape.T, shape.H).to(DEV)
     off = MI.load_zipf_offsets(shape.E).to(DEV) if shape.offset == "zipf" else None
-    y, ids, w, counts = bm.block(x, wr, wg, wu, wd, shape.groups, shape.topk_groups, shape.k,
+    y, ids, w, counts = bm.block(x, wr, *packed, shape.groups, shape.topk_groups, shape.k,
                                  shape.scale, logit_offset=off)
     sync()
     ref_r = oracle_route(x, wr, shape, off)
@@ -92,12 +93,13 @@ def test_beam_stack_T4096_four_sublayers(bm, beam_weights):
         step = layer + 2
         print(f"[case] stack layer {layer} step {step}", flush=True)
         if layer == 0:
-            wr, wg, wu, wd = beam_weights
+            wr, wg, wu, wd, packed = beam_weights
         else:
             wr = MI.make_router(shape.E, shape.H, layer=layer).to(DEV)
             wg, wu, wd = MI.make_expert_weights(shape.E, shape.H, shape.I, DEV, layer=layer)
+            packed = bm.pack_experts(wg, wu, wd)
         prev = stream.clone()
-        xin, yb, ids, w, counts = bm.sublayer(stream, step, wr, wg, wu, wd)
+        xin, yb, ids, w, counts = bm.sublayer(stream, step, wr, *packed)
         sync()
         prev64 = prev.cpu().numpy().astype(np.float64)
         got_in = O.bf16_bits_to_f64(bf16_bits(xin))
@@ -113,5 +115,5 @@ def test_beam_stack_T4096_four_sublayers(bm, beam_weights):
         np.testing.assert_allclose(stream.cpu().numpy(), ref_stream, rtol=1e-5, atol=1e-5)
         print({k: v for k, v in st.items() if k != "excluded_tokens"}, flush=True)
         if layer > 0:
-            del wg, wu, wd
+            del wg, wu, wd, packed
             torch.cuda.empty_cache()

@@ -33,8 +33,8 @@ def oracle_full(inp, shape):
 
 
 def run_block(bm, inp, shape):
-    out = bm.block(inp.x, inp.wr, inp.wg, inp.wu, inp.wd, shape.groups, shape.topk_groups,
-                   shape.k, shape.scale, logit_offset=inp.offset)
+    out = bm.block(inp.x, inp.wr, *bm.pack_experts(inp.wg, inp.wu, inp.wd), shape.groups,
+                   shape.topk_groups, shape.k, shape.scale, logit_offset=inp.offset)
     sync()
     return out
 
@@ -95,6 +95,50 @@ def test_block_larger_dims_tiled(bm):
             bm.set_schedule("auto")
 
 
+@pytest.mark.parametrize("schedule", ["stream", "tiled"])
+def test_block_padded_rows(bm, schedule):
+    """H = 320, I = 192: neither is a multiple of the 128-row packed block, so
+    both GEMMs read zero-padded rows, and K is 64 past a multiple of 128 (the
+    streaming schedule's tail step)."""
+    shape = BlockShape(T=300, H=320, I=192)
+    inp = MI.make_block_inputs(shape, DEV, case=11)
+    bm.set_schedule(schedule)
+    try:
+        y, ids, w, counts = run_block(bm, inp, shape)
+    finally:
+        bm.set_schedule("auto")
+    ref = oracle_full(inp, shape)
+    st = check_routing(ids, w, ref, shape.E, counts)
+    st.update(check_output(y, ref["y"], keep_mask(ref)))
+
+
+def pack_layout_reference(bits):
+    """The packed block layout written out with numpy index arithmetic: rows
+    padded to a multiple of 128, blocks of 128 rows x 32 k in (row block,
+    k-block) order, 16-byte chunk c of block row j stored at c ^ swz(j)."""
+    E, N, K = bits.shape
+    NB, KB = -(-N // 128), K // 32
+    pad = np.zeros((E, NB * 128, K), np.uint16)
+    pad[:, :N] = bits
+    blocks = pad.reshape(E, NB, 128, KB, 4, 8).transpose(0, 1, 3, 2, 4, 5)  # e, rb, kb, j, c, 8
+    j = np.arange(128)[:, None]
+    swz = ((j >> 1) ^ (j >> 2)) & 3
+    logical = np.arange(4)[None, :] ^ swz          # physical slot p holds logical chunk p ^ swz
+    out = blocks[:, :, :, np.arange(128)[:, None], logical, :]
+    return out.reshape(-1)
+
+
+@pytest.mark.parametrize("E,N,K", [(3, 192, 128), (2, 256, 320), (1, 64, 64)])
+def test_pack_layout_bit_exact(bm, E, N, K):
+    g = torch.Generator(device="cpu").manual_seed(E * 1000 + N + K)
+    w = torch.randn(E, N, K, generator=g).to(torch.bfloat16).to(DEV)
+    packed = bm.pack_weights(w)
+    sync()
+    assert packed.data.numel() == E * bm.packed_weight_bytes(N, K)
+    got = packed.data.cpu().numpy().view(np.uint16)
+    assert np.array_equal(got, pack_layout_reference(bf16_bits(w)))
+
+
 def test_block_k1(bm):
     shape = BlockShape(T=96, H=256, I=128, k=1)
     inp, ref, (y, ids, w, counts) = full_check(bm, shape, case=3, out_rounding_slack=True)
@@ -131,10 +175,11 @@ def test_forward_injected_one_hot_and_dropped_ids(bm):
     w[1::2, 1] = 0.5
     ids_t = torch.from_numpy(ids).to(DEV)
     w_t = torch.from_numpy(w).to(DEV)
+    packed = bm.pack_experts(inp.wg, inp.wu, inp.wd)
     for schedule in ("stream", "tiled"):
         bm.set_schedule(schedule)
         try:
-            y, counts = bm.forward(inp.x, ids_t, w_t, inp.wg, inp.wu, inp.wd, return_counts=True)
+            y, counts = bm.forward(inp.x, ids_t, w_t, *packed, return_counts=True)
             sync()
         finally:
             bm.set_schedule("auto")
@@ -151,7 +196,7 @@ def test_forward_single_expert_is_scale_times_swiglu(bm):
     inp = MI.make_block_inputs(shape, DEV, case=8)
     ids = torch.full((64, 1), 17, dtype=torch.int32, device=DEV)
     w = torch.full((64, 1), 2.5, dtype=torch.float32, device=DEV)
-    y = bm.forward(inp.x, ids, w, inp.wg, inp.wu, inp.wd)
+    y = bm.forward(inp.x, ids, w, *bm.pack_experts(inp.wg, inp.wu, inp.wd))
     sync()
     xf = O.bf16_bits_to_f64(bf16_bits(inp.x))
     ref = 2.5 * O.swiglu_expert(xf, O.bf16_bits_to_f64(bf16_bits(inp.wg[17])),
@@ -172,7 +217,7 @@ def test_block_T0(bm):
     shape = BlockShape(T=0, H=256, I=128)
     inp = MI.make_block_inputs(BlockShape(T=4, H=256, I=128), DEV)
     x0 = inp.x[:0]
-    y, ids, w, counts = bm.block(x0, inp.wr, inp.wg, inp.wu, inp.wd)
+    y, ids, w, counts = bm.block(x0, inp.wr, *bm.pack_experts(inp.wg, inp.wu, inp.wd))
     sync()
     assert y.shape == (0, 256) and ids.shape == (0, 8)
 
@@ -225,7 +270,7 @@ def test_sublayer_tiny_teacher_forced(bm):
         wr = MI.make_router(shape.E, shape.H, layer=layer, case=10).to(DEV)
         wg, wu, wd = MI.make_expert_weights(shape.E, shape.H, shape.I, DEV, layer=layer, case=10)
         prev = stream.clone()
-        xin, yb, ids, w, counts = bm.sublayer(stream, step, wr, wg, wu, wd)
+        xin, yb, ids, w, counts = bm.sublayer(stream, step, wr, *bm.pack_experts(wg, wu, wd))
         sync()
         prev64 = prev.cpu().numpy().astype(np.float64)
         # MoE input = bf16(RMSNorm(stream)), within one bf16 ulp
