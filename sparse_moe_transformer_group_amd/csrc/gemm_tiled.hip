@@ -151,6 +151,7 @@ __global__ __launch_bounds__(256, OCC) void grouped_tiled_kernel(GroupedArgs a) 
   const int nk = K / kBK;
   const uint32_t wbytes = (uint32_t)packed_expert_bytes(N, K);  // one packed expert matrix (< 2^31)
   const __amdgpu_buffer_rsrc_t rs_act = buf_rsrc(a.act, 0x7fffffffu);
+  const uint32_t tk64 = (uint32_t)a.Tk * 64u;  // one k-block of the k-major h
   const uint32_t ring_lds = (uint32_t)(uintptr_t)(lds_void*)ring;
 
   // Per-lane byte offsets inside a stage (same for every stage).  The chunk
@@ -238,8 +239,16 @@ __global__ __launch_bounds__(256, OCC) void grouped_tiled_kernel(GroupedArgs a) 
         const int trow = 16 * (4 * q + wave) + lrow;
         const int tok = min(m0 + trow, m1 - 1);
         const int rr = row0 + tok;
-        const uint32_t src = a.sorted_tokens ? (uint32_t)a.sorted_tokens[rr] : (uint32_t)rr;
-        toff[q] = src * (uint32_t)K * 2u + (rchunk(trow, lpc) << 4);
+        if constexpr (MAT == 2) {
+          // x rows (row-major, gathered through sorted_tokens)
+          const uint32_t src = (uint32_t)a.sorted_tokens[rr];
+          toff[q] = src * (uint32_t)K * 2u + (rchunk(trow, lpc) << 4);
+        } else {
+          // h in k-major order (written so by the gate/up epilogue): row rr
+          // of k-block kb at (kb * Tk + rr) * 64, chunks swizzled by rr; the
+          // lane fetches the chunk that belongs in LDS slot lpc of row trow.
+          toff[q] = (uint32_t)rr * 64u + ((lpc ^ pack_swz(trow) ^ pack_swz(rr)) << 4);
+        }
       }
 
       f32x16 acc[2][NB];
@@ -254,9 +263,9 @@ __global__ __launch_bounds__(256, OCC) void grouped_tiled_kernel(GroupedArgs a) 
         if (d < 4)  // weights: k-block kt of the packed block, so * 128 = kt * 8 KB
           dma16(__builtin_amdgcn_readfirstlane(st + w_base + 16 * d * 64), woff[d],
                 (MAT == 2 && d >= 2) ? rs_w1 : rs_w0, so * (kPackBlockBytes / (kBK * 2)));
-        else
+        else  // tokens: x step offset kt * 64, or k-major h block kt * Tk * 64
           dma16(__builtin_amdgcn_readfirstlane(st + kWBytes + 16 * (4 * (d - 4) + wave) * 64),
-                toff[d - 4], rs_act, so);
+                toff[d - 4], rs_act, (MAT == 2) ? so : (so >> 6) * tk64);
       };
       auto issue = [&](int kt) {  // loads of step kt into stage kt % STAGES
         const uint32_t st = ring_lds + (kt % STAGES) * Stage;
@@ -337,13 +346,18 @@ __global__ __launch_bounds__(256, OCC) void grouped_tiled_kernel(GroupedArgs a) 
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) {
           if constexpr (MAT == 2) {
+            // h k-major: feature f of row `row` sits in k-block f/32, chunk
+            // (f%32)/8 (swizzled by the row), element f%8; the 4 features
+            // f..f+3 share one chunk.
             const int f = fw + 8 * q4 + 4 * g;
             if (f >= N) continue;
             uint32_t p[4];
 #pragma unroll
             for (int c = 0; c < 4; ++c)
               p[c] = f32_to_bf16_rne(swiglu(acc[0][j][4 * q4 + c], acc[1][j][4 * q4 + c]));
-            *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + row * N + f) =
+            const int64_t off = ((int64_t)(f >> 5) * a.Tk + row) * 32 +
+                                ((((f & 31) >> 3) ^ pack_swz((int)row)) << 3) + (f & 7);
+            *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + off) =
                 make_uint2(p[0] | (p[1] << 16), p[2] | (p[3] << 16));
           } else {
 #pragma unroll

@@ -45,13 +45,14 @@ hipError_t launch_pack(hipStream_t s, const uint16_t* src, uint16_t* dst, int E,
 
 // ---- grouped expert GEMMs (gemm_stream.hip, gemm_tiled.hip) ----
 struct GroupedArgs {
-  const uint16_t* act;          // activations: x [T,H] (gate/up) or h [Tk,I] (down)
+  const uint16_t* act;          // activations: x [T,H] (gate/up) or h (down): [Tk,I] row-major
+                                // on the stream path, k-major on the tiled path (see gemm_tiled.hip)
   const int32_t* sorted_tokens; // row indirection for x (gate/up); NULL for h
   const uint16_t* w0;           // packed gate [E,I,H] or down [E,H,I]
   const uint16_t* w1;           // packed up [E,I,H] or NULL
   const int32_t* counts;        // [E]
   const int32_t* offsets;       // [E+1]
-  void* out;                    // h [Tk,I] bf16 or o [Tk,H] fp32
+  void* out;                    // h bf16 (layout as for act) or o [Tk,H] fp32
   int N;                        // output features (I or H)
   int K;                        // reduction length (H or I)
   int E;
