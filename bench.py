@@ -7,7 +7,7 @@ of synthetic tokens, with inputs and weights already resident in HBM.
 
 Default workload: the Beam-shape decode batch (T=64, hidden 5120,
 intermediate 2560, 256 experts, 8 groups / keep 4 / top-8, x2.5), where
-reading the chosen experts' weights dominates.  --workload prefill|skewed|
+reading the chosen experts' weights dominates.  --workload verify|prefill|skewed|
 stack|tiny measures the other shapes.
 
 Prints one JSON line.  `roofline` describes the dominant kernel (gate/up):
@@ -47,7 +47,7 @@ def parse():
     p.add_argument("--steps", type=int, default=None)
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--workload", default="decode",
-                   choices=["decode", "prefill", "skewed", "stack", "tiny"])
+                   choices=["decode", "verify", "prefill", "skewed", "stack", "tiny"])
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-sample-tokens", type=int, default=None)
     p.add_argument("--copy-probe", action="store_true",
@@ -89,7 +89,7 @@ def main():
     dev = torch.device("cuda:0")
     shape = MI.WORKLOADS[args.workload]
     steps = args.steps if args.steps is not None else (
-        {"decode": 100, "tiny": 200}.get(args.workload, 20))
+        {"decode": 100, "verify": 50, "tiny": 200}.get(args.workload, 20))
     T, H, I, E, k = shape.T, shape.H, shape.I, shape.E, shape.k
     layers = shape.layers
 
@@ -176,7 +176,7 @@ def main():
         ach = gu_flops / (gu_ms * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4)}
-    schedule = "stream" if T * k <= 32 * E else "tiled"
+    schedule = "stream" if T * k < 20 * E else "tiled"
     roof["traffic"] = measured_traffic(args.workload, schedule)
     roof["kernel"] = "grouped_stream_kernel<2,1,*> (gate/up)" if schedule == "stream" else \
         "grouped_tiled_kernel<2,...> (gate/up)"

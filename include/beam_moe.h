@@ -183,7 +183,7 @@ int beam_moe_sublayer(void* stream, int64_t T, int H, int I, int E, int groups, 
 
 /*
  * Expert-GEMM schedule for later calls in this process: 0 = automatic (the
- * weight-streaming schedule when there are at most ~32 assignments per
+ * weight-streaming schedule when there are fewer than 20 assignments per
  * expert on average, the LDS-tiled schedule otherwise), 1 = always
  * streaming, 2 = always tiled.  Both give the same results up to FP32
  * summation order inside the MFMA accumulations.  Returns INVALID_DIM for

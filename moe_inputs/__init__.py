@@ -66,6 +66,11 @@ WORKLOADS = {
     "tiny": BlockShape(T=128, H=256, I=128, name="tiny"),
     # Beam shape, decode-size batch: expert-weight streaming
     "decode": BlockShape(T=64, H=5120, I=2560, name="decode"),
+    # Beam shape, speculative-verify batch: 16 sequences x 16 tokens (a
+    # drafter proposes up to 15 tokens and the model checks them plus the
+    # current one in a single forward pass; page "Reflection 发布 501B 开放模型
+    # Beam，支持自托管定制与扩展" (sihot.dev), section vLLM)
+    "verify": BlockShape(T=256, H=5120, I=2560, name="verify"),
     # Beam shape, prefill chunk with near-uniform load
     "prefill": BlockShape(T=8192, H=5120, I=2560, name="prefill"),
     # Beam shape, Zipf(1.1)-skewed expert load through per-expert logit offsets

@@ -74,6 +74,10 @@ def test_beam_decode_T64(bm, beam_weights):
     beam_case(bm, beam_weights, "decode")
 
 
+def test_beam_verify_T256(bm, beam_weights):
+    beam_case(bm, beam_weights, "verify")
+
+
 def test_beam_prefill_T8192(bm, beam_weights):
     beam_case(bm, beam_weights, "prefill")
 
