@@ -6,3 +6,4 @@ binding) never imports, calls or links anything here, and nothing here
 imports the product path.
 """
 from .beam_moe_oracle import *  # noqa: F401,F403
+from .fp8_weights import *  # noqa: F401,F403

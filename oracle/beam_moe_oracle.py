@@ -234,12 +234,20 @@ ExpertSource = Union[Tuple[np.ndarray, np.ndarray, np.ndarray],
                      Callable[[int], Tuple[np.ndarray, np.ndarray, np.ndarray]]]
 
 
+def _widen(w):
+    """bf16 bit patterns -> float64; float64 weights (already dequantised,
+    e.g. FP8-encoded experts) pass through unchanged."""
+    w = np.asarray(w)
+    return w if w.dtype == np.float64 else bf16_bits_to_f64(w)
+
+
 def _expert_getter(experts: ExpertSource):
-    """Per-expert float64 weights from bf16-bit arrays or a callable."""
+    """Per-expert float64 weights from bf16-bit arrays or a callable (which
+    may also return float64 weights)."""
     if callable(experts):
         def get(e):
             wg, wu, wd = experts(e)
-            return bf16_bits_to_f64(wg), bf16_bits_to_f64(wu), bf16_bits_to_f64(wd)
+            return _widen(wg), _widen(wu), _widen(wd)
         return get
     wg_b, wu_b, wd_b = experts
 
