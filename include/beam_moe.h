@@ -91,6 +91,29 @@ size_t beam_moe_packed_weight_bytes(int N, int K);
 int beam_moe_pack_weights(void* stream, int E, int N, int K, const uint16_t* src, uint16_t* dst);
 
 /*
+ * FP8 expert weights (OCP E4M3), for the *_fp8 compute calls.  The pages
+ * state that an FP8 checkpoint of the model exists ([MoE]; section on
+ * hardware requirements) but not its scaling; this library's encoding is:
+ *   - one scale per output row r of each expert matrix: 2^e_r with e_r the
+ *     smallest integer such that max_k |W[r,k]| <= 448 * 2^e_r (e_r = 0 for
+ *     an all-zero row); scales[e][r] holds 2^e_r as fp32;
+ *   - code[r,k] = the E4M3 value nearest to W[r,k] * 2^-e_r, ties to the even
+ *     mantissa (the scaling by a power of two is exact); the weight the
+ *     kernels use is value(code) * 2^e_r;
+ *   - layout: the packed block grid above with one byte per weight: blocks of
+ *     128 rows x 32 k = 4096 bytes at (rb * K/32 + kb) * 4096; row j takes
+ *     32 bytes at j*32; its 8-byte chunk c (k = kb*32 + 8c .. + 7) is stored
+ *     at chunk position c XOR ((j >> 3) AND 3); rows past N are zero.
+ * beam_moe_packed_fp8_bytes: bytes of one packed N x K FP8 expert matrix (0
+ *   if the sizes break the rule above).
+ * beam_moe_pack_weights_fp8: dst [E * packed bytes] and scales [E,N] fp32
+ *   from src [E,N,K] bf16 (finite values).  No two of the buffers may overlap.
+ */
+size_t beam_moe_packed_fp8_bytes(int N, int K);
+int beam_moe_pack_weights_fp8(void* stream, int E, int N, int K, const uint16_t* src,
+                              uint8_t* dst, float* scales);
+
+/*
  * Router + group-limited top-k  ([MoE]; router in FP32 per [RES]).
  *   z[t,e]  = sum_h x[t,h] * w_router[e,h]  (+ logit_offset[e])   FP32 accumulate
  *   s[t,e]  = 1 / (1 + exp(-z[t,e]))                               FP32
@@ -152,6 +175,26 @@ int beam_moe_block(void* stream, int64_t T, int H, int I, int E, int groups, int
                    const float* logit_offset, const uint16_t* w_gate, const uint16_t* w_up,
                    const uint16_t* w_down, uint16_t* y, int32_t* topk_ids, float* topk_weights,
                    int32_t* expert_counts, void* workspace, size_t workspace_bytes);
+
+/*
+ * The same two calls with FP8 expert weights (see beam_moe_pack_weights_fp8):
+ * w_* are the packed E4M3 codes and s_* the [E,N] fp32 row scales of gate,
+ * up and down.  Each expert computes with the weights value(code) * scale
+ * (dequantised exactly to bf16 operands, the scale applied to the FP32
+ * accumulators); everything else is as in forward / block.
+ */
+int beam_moe_forward_fp8(void* stream, int64_t T, int H, int I, int E, int k, const uint16_t* x,
+                         const int32_t* topk_ids, const float* topk_weights,
+                         const uint8_t* w_gate, const float* s_gate, const uint8_t* w_up,
+                         const float* s_up, const uint8_t* w_down, const float* s_down,
+                         uint16_t* y, int32_t* expert_counts, void* workspace,
+                         size_t workspace_bytes);
+int beam_moe_block_fp8(void* stream, int64_t T, int H, int I, int E, int groups, int topk_groups,
+                       int k, float scale, const uint16_t* x, const uint16_t* w_router,
+                       const float* logit_offset, const uint8_t* w_gate, const float* s_gate,
+                       const uint8_t* w_up, const float* s_up, const uint8_t* w_down,
+                       const float* s_down, uint16_t* y, int32_t* topk_ids, float* topk_weights,
+                       int32_t* expert_counts, void* workspace, size_t workspace_bytes);
 
 /*
  * Residual stream helpers  ([RES]: every sublayer is normalised before and

@@ -6,8 +6,9 @@ ABI declared in include/beam_moe.h; this package is its ctypes binding.
 Importing it fails if the library has not been built.
 """
 from ._lib import (  # noqa: F401
-    BeamMoeError, PackedMatrix, StageTimer, block, forward, get_workspace, lib, pack_experts,
-    pack_weights, packed_weight_bytes, permute, release_workspaces, residual_update, rmsnorm, route,
+    BeamMoeError, PackedFP8, PackedMatrix, StageTimer, block, forward, get_workspace, lib,
+    pack_experts, pack_experts_fp8, pack_weights, pack_weights_fp8, packed_fp8_bytes,
+    packed_weight_bytes, permute, release_workspaces, residual_update, rmsnorm, route,
     set_schedule, stage_names, stream_init, sublayer, version, workspace_bytes,
 )
 from .build import LIB_PATH  # noqa: F401

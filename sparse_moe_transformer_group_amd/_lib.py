@@ -42,6 +42,8 @@ def _load():
         "beam_moe_workspace_bytes": (_c_sz, [_c_i64, _c_int, _c_int, _c_int, _c_int]),
         "beam_moe_packed_weight_bytes": (_c_sz, [_c_int, _c_int]),
         "beam_moe_pack_weights": (_c_int, [_c_vp, _c_int, _c_int, _c_int, _c_vp, _c_vp]),
+        "beam_moe_packed_fp8_bytes": (_c_sz, [_c_int, _c_int]),
+        "beam_moe_pack_weights_fp8": (_c_int, [_c_vp, _c_int, _c_int, _c_int, _c_vp, _c_vp, _c_vp]),
         "beam_moe_route": (_c_int, [_c_vp, _c_i64, _c_int, _c_int, _c_int, _c_int, _c_int, _c_f,
                                     _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_sz]),
         "beam_moe_permute": (_c_int, [_c_vp, _c_i64, _c_int, _c_int, _c_vp, _c_vp, _c_vp, _c_vp,
@@ -51,6 +53,13 @@ def _load():
         "beam_moe_block": (_c_int, [_c_vp, _c_i64, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
                                     _c_f, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp,
                                     _c_vp, _c_vp, _c_vp, _c_sz]),
+        "beam_moe_forward_fp8": (_c_int, [_c_vp, _c_i64, _c_int, _c_int, _c_int, _c_int, _c_vp,
+                                          _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp,
+                                          _c_vp, _c_vp, _c_vp, _c_vp, _c_sz]),
+        "beam_moe_block_fp8": (_c_int, [_c_vp, _c_i64, _c_int, _c_int, _c_int, _c_int, _c_int,
+                                        _c_int, _c_f, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp,
+                                        _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp,
+                                        _c_sz]),
         "beam_moe_stream_init": (_c_int, [_c_vp, _c_i64, _c_int, _c_vp, _c_vp]),
         "beam_moe_rmsnorm": (_c_int, [_c_vp, _c_i64, _c_int, _c_f, _c_vp, _c_vp]),
         "beam_moe_residual_update": (_c_int, [_c_vp, _c_i64, _c_int, _c_f, _c_int, _c_vp, _c_vp]),
@@ -222,15 +231,59 @@ def pack_weights(w: torch.Tensor) -> PackedMatrix:
     return PackedMatrix(out, E, N, K)
 
 
+class PackedFP8:
+    """E expert matrices of N x K as FP8 (E4M3) codes in the packed block
+    layout plus one fp32 power-of-two scale per row (beam_moe_pack_weights_fp8)."""
+
+    __slots__ = ("data", "scales", "E", "N", "K")
+
+    def __init__(self, data: torch.Tensor, scales: torch.Tensor, E: int, N: int, K: int):
+        self.data, self.scales, self.E, self.N, self.K = data, scales, E, N, K
+
+    @property
+    def shape(self):
+        return (self.E, self.N, self.K)
+
+    @property
+    def device(self):
+        return self.data.device
+
+
+def packed_fp8_bytes(N: int, K: int) -> int:
+    """Bytes of one packed N x K FP8 expert matrix."""
+    n = lib.beam_moe_packed_fp8_bytes(int(N), int(K))
+    if n == 0:
+        raise ValueError(f"unsupported matrix shape {N} x {K} (multiples of 64 up to 32768)")
+    return n
+
+
+def pack_weights_fp8(w: torch.Tensor) -> PackedFP8:
+    """FP8 codes + row scales of expert matrices w [E, N, K] bf16."""
+    E, N, K = w.shape
+    _dev_tensor(w, "w", torch.bfloat16, (E, N, K))
+    out = torch.empty((E * packed_fp8_bytes(N, K),), dtype=torch.uint8, device=w.device)
+    sc = torch.empty((E, N), dtype=torch.float32, device=w.device)
+    _check("beam_moe_pack_weights_fp8",
+           lib.beam_moe_pack_weights_fp8(_stream(w.device), E, N, K, _ptr(w), _ptr(out), _ptr(sc)))
+    return PackedFP8(out, sc, E, N, K)
+
+
+def pack_experts_fp8(w_gate, w_up, w_down):
+    """(gate, up, down) as FP8 for the *_fp8 compute calls."""
+    return pack_weights_fp8(w_gate), pack_weights_fp8(w_up), pack_weights_fp8(w_down)
+
+
 def pack_experts(w_gate, w_up, w_down):
     """(gate, up, down) in the packed layout the compute calls take."""
     return pack_weights(w_gate), pack_weights(w_up), pack_weights(w_down)
 
 
-def _expert_shapes(w_gate, w_up, w_down):
+def _expert_shapes(w_gate, w_up, w_down, allow_fp8=True):
+    kind = PackedFP8 if isinstance(w_gate, PackedFP8) and allow_fp8 else PackedMatrix
     for name, m in (("w_gate", w_gate), ("w_up", w_up), ("w_down", w_down)):
-        if not isinstance(m, PackedMatrix):
-            raise TypeError(f"{name} must be packed with pack_weights / pack_experts")
+        if not isinstance(m, kind):
+            raise TypeError(f"{name} must be packed with pack_weights / pack_experts"
+                            + (" or pack_experts_fp8 (all three alike)" if allow_fp8 else ""))
         if not m.data.is_cuda:
             raise ValueError(f"{name} must be a device buffer")
     E, I, H = w_gate.shape
@@ -252,9 +305,17 @@ def forward(x, topk_ids, topk_weights, w_gate, w_up, w_down, return_counts=False
     y = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
     counts = torch.empty((E,), dtype=torch.int32, device=dev) if return_counts else None
     ws = get_workspace(dev, workspace_bytes(T, H, I, E, k))
+    if isinstance(w_gate, PackedFP8):
+        rc = lib.beam_moe_forward_fp8(_stream(dev), T, H, I, E, k, _ptr(x), _ptr(topk_ids),
+                                      _ptr(topk_weights), _ptr(w_gate.data), _ptr(w_gate.scales),
+                                      _ptr(w_up.data), _ptr(w_up.scales), _ptr(w_down.data),
+                                      _ptr(w_down.scales), _ptr(y), _ptr(counts), _ptr(ws),
+                                      ws.numel())
+        _check("beam_moe_forward_fp8", rc)
+        return (y, counts) if return_counts else y
     rc = lib.beam_moe_forward(_stream(dev), T, H, I, E, k, _ptr(x), _ptr(topk_ids),
-                              _ptr(topk_weights), _ptr(w_gate.data), _ptr(w_up.data), _ptr(w_down.data), _ptr(y),
-                              _ptr(counts), _ptr(ws), ws.numel())
+                              _ptr(topk_weights), _ptr(w_gate.data), _ptr(w_up.data),
+                              _ptr(w_down.data), _ptr(y), _ptr(counts), _ptr(ws), ws.numel())
     _check("beam_moe_forward", rc)
     return (y, counts) if return_counts else y
 
@@ -278,6 +339,14 @@ def block(x, w_router, w_gate, w_up, w_down, groups=8, topk_groups=4, k=8, scale
         w = torch.empty((T, k), dtype=torch.float32, device=dev)
         counts = torch.empty((E,), dtype=torch.int32, device=dev)
     ws = get_workspace(dev, workspace_bytes(T, H, I, E, k))
+    if isinstance(w_gate, PackedFP8):
+        rc = lib.beam_moe_block_fp8(_stream(dev), T, H, I, E, groups, topk_groups, k, float(scale),
+                                    _ptr(x), _ptr(w_router), _ptr(logit_offset), _ptr(w_gate.data),
+                                    _ptr(w_gate.scales), _ptr(w_up.data), _ptr(w_up.scales),
+                                    _ptr(w_down.data), _ptr(w_down.scales), _ptr(y), _ptr(ids),
+                                    _ptr(w), _ptr(counts), _ptr(ws), ws.numel())
+        _check("beam_moe_block_fp8", rc)
+        return (y, ids, w, counts) if return_routing else y
     rc = lib.beam_moe_block(_stream(dev), T, H, I, E, groups, topk_groups, k, float(scale), _ptr(x),
                             _ptr(w_router), _ptr(logit_offset), _ptr(w_gate.data), _ptr(w_up.data),
                             _ptr(w_down.data), _ptr(y), _ptr(ids), _ptr(w), _ptr(counts), _ptr(ws),
@@ -314,9 +383,10 @@ def residual_update(stream_io, y, step, eps=1e-6):
 
 def sublayer(stream_io, step, w_router, w_gate, w_up, w_down, groups=8, topk_groups=4, k=8,
              scale=2.5, eps=1e-6, keep_io=True):
-    """One sandwich-normed MoE sublayer + residual update, in place on stream_io.
-    Returns (moe_input, moe_output, ids, weights, counts) when keep_io."""
-    E, I, H = _expert_shapes(w_gate, w_up, w_down)
+    """One sandwich-normed MoE sublayer + residual update, in place on stream_io
+    (bf16 packed expert weights).  Returns (moe_input, moe_output, ids, weights,
+    counts) when keep_io."""
+    E, I, H = _expert_shapes(w_gate, w_up, w_down, allow_fp8=False)
     T = stream_io.shape[0]
     dev = stream_io.device
     _dev_tensor(stream_io, "stream", torch.float32, (T, H))

@@ -221,10 +221,16 @@ int run_permute(hipStream_t st, int64_t T, int E, int k, const int32_t* ids, int
   return BEAM_MOE_OK;
 }
 
+// Expert weights as the kernels take them: packed bf16 (scales NULL) or
+// packed FP8 codes with per-row scales.
+struct Experts {
+  const uint16_t *wg, *wu, *wd;
+  const float *sg, *su, *sd;
+};
+
 int run_forward(hipStream_t st, int64_t T, int H, int I, int E, int k, const uint16_t* x,
-                const int32_t* ids, const float* w, const uint16_t* wg, const uint16_t* wu,
-                const uint16_t* wd, uint16_t* y, int32_t* user_counts, const Layout& L, char* ws,
-                int slot, int num_cu) {
+                const int32_t* ids, const float* w, const Experts& ex, uint16_t* y,
+                int32_t* user_counts, const Layout& L, char* ws, int slot, int num_cu) {
   const int64_t Tk = T * k;
   int32_t* counts = reinterpret_cast<int32_t*>(ws + L.counts);
   int32_t* offsets = reinterpret_cast<int32_t*>(ws + L.offsets);
@@ -240,12 +246,12 @@ int run_forward(hipStream_t st, int64_t T, int H, int I, int E, int k, const uin
   const bool stream = use_stream(T, H, I, k, E);
   {
     StageScope sc(slot, ST_GATEUP, st);
-    GroupedArgs a{x, sorted, wg, wu, counts, offsets, h, I, H, E, Tk};
+    GroupedArgs a{x, sorted, ex.wg, ex.wu, ex.sg, ex.su, counts, offsets, h, I, H, E, Tk};
     BEAM_TRY(stream ? launch_gateup_stream(st, a, T, k) : launch_gateup_tiled(st, a, num_cu));
   }
   {
     StageScope sc(slot, ST_DOWN, st);
-    GroupedArgs a{h, nullptr, wd, nullptr, counts, offsets, o, H, I, E, Tk};
+    GroupedArgs a{h, nullptr, ex.wd, nullptr, ex.sd, nullptr, counts, offsets, o, H, I, E, Tk};
     BEAM_TRY(stream ? launch_down_stream(st, a, T, k) : launch_down_tiled(st, a, num_cu));
   }
   {
@@ -295,6 +301,31 @@ int beam_moe_pack_weights(void* stream, int E, int N, int K, const uint16_t* src
   if ((rc = device_check(&num_cu))) return rc;
   return launch_pack((hipStream_t)stream, src, dst, E, N, K) == hipSuccess ? BEAM_MOE_OK
                                                                            : BEAM_MOE_ERR_HIP;
+}
+
+size_t beam_moe_packed_fp8_bytes(int N, int K) {
+  if (bad_dim64(N) || bad_dim64(K)) return 0;
+  return (size_t)packed8_expert_bytes(N, K);
+}
+
+int beam_moe_pack_weights_fp8(void* stream, int E, int N, int K, const uint16_t* src,
+                              uint8_t* dst, float* scales) {
+  if (E < 1 || E > kMaxE || bad_dim64(N) || bad_dim64(K)) return BEAM_MOE_ERR_INVALID_DIM;
+  int rc = check_ptrs({src, dst, scales}, {});
+  if (rc) return rc;
+  const char* s0 = reinterpret_cast<const char*>(src);
+  const int64_t sb = (int64_t)E * N * K * 2;
+  const char* d0 = reinterpret_cast<const char*>(dst);
+  const int64_t db = (int64_t)E * packed8_expert_bytes(N, K);
+  const char* c0 = reinterpret_cast<const char*>(scales);
+  const int64_t cb = (int64_t)E * N * 4;
+  if ((s0 < d0 + db && d0 < s0 + sb) || (s0 < c0 + cb && c0 < s0 + sb) || (d0 < c0 + cb && c0 < d0 + db))
+    return BEAM_MOE_ERR_INVALID_DIM;
+  int num_cu;
+  if ((rc = device_check(&num_cu))) return rc;
+  return launch_pack_fp8((hipStream_t)stream, src, dst, scales, E, N, K) == hipSuccess
+             ? BEAM_MOE_OK
+             : BEAM_MOE_ERR_HIP;
 }
 
 size_t beam_moe_workspace_bytes(int64_t T, int H, int I, int E, int k) {
@@ -349,22 +380,51 @@ int beam_moe_forward(void* stream, int64_t T, int H, int I, int E, int k, const 
   int num_cu;
   if ((rc = device_check(&num_cu))) return rc;
   const int slot = timer_claim();
-  return run_forward((hipStream_t)stream, T, H, I, E, k, x, topk_ids, topk_weights, w_gate, w_up,
-                     w_down, y, expert_counts, L, static_cast<char*>(workspace), slot, num_cu);
+  const Experts ex{w_gate, w_up, w_down, nullptr, nullptr, nullptr};
+  return run_forward((hipStream_t)stream, T, H, I, E, k, x, topk_ids, topk_weights, ex, y,
+                     expert_counts, L, static_cast<char*>(workspace), slot, num_cu);
 }
 
-int beam_moe_block(void* stream, int64_t T, int H, int I, int E, int groups, int topk_groups, int k,
-                   float scale, const uint16_t* x, const uint16_t* w_router,
-                   const float* logit_offset, const uint16_t* w_gate, const uint16_t* w_up,
-                   const uint16_t* w_down, uint16_t* y, int32_t* topk_ids, float* topk_weights,
-                   int32_t* expert_counts, void* workspace, size_t workspace_bytes) {
+int beam_moe_forward_fp8(void* stream, int64_t T, int H, int I, int E, int k, const uint16_t* x,
+                         const int32_t* topk_ids, const float* topk_weights,
+                         const uint8_t* w_gate, const float* s_gate, const uint8_t* w_up,
+                         const float* s_up, const uint8_t* w_down, const float* s_down,
+                         uint16_t* y, int32_t* expert_counts, void* workspace,
+                         size_t workspace_bytes) {
+  int rc = check_forward_dims(T, H, I, E, k);
+  if (rc) return rc;
+  if (T == 0) return BEAM_MOE_OK;
+  rc = check_ptrs({x, topk_ids, topk_weights, w_gate, s_gate, w_up, s_up, w_down, s_down, y,
+                   workspace},
+                  {expert_counts});
+  if (rc) return rc;
+  const Layout L = layout(T, H, I, E, k);
+  if (workspace_bytes < L.total) return BEAM_MOE_ERR_WORKSPACE_TOO_SMALL;
+  int num_cu;
+  if ((rc = device_check(&num_cu))) return rc;
+  const int slot = timer_claim();
+  const Experts ex{reinterpret_cast<const uint16_t*>(w_gate), reinterpret_cast<const uint16_t*>(w_up),
+                   reinterpret_cast<const uint16_t*>(w_down), s_gate, s_up, s_down};
+  return run_forward((hipStream_t)stream, T, H, I, E, k, x, topk_ids, topk_weights, ex, y,
+                     expert_counts, L, static_cast<char*>(workspace), slot, num_cu);
+}
+
+}  // extern "C"
+
+namespace {
+int block_common(void* stream, int64_t T, int H, int I, int E, int groups, int topk_groups, int k,
+                 float scale, const uint16_t* x, const uint16_t* w_router,
+                 const float* logit_offset, const Experts& ex, uint16_t* y, int32_t* topk_ids,
+                 float* topk_weights, int32_t* expert_counts, void* workspace,
+                 size_t workspace_bytes) {
   int rc = check_route_dims(T, H, E, groups, topk_groups, k, scale);
   if (rc) return rc;
   if ((rc = check_forward_dims(T, H, I, E, k))) return rc;
   if (T == 0) return BEAM_MOE_OK;
-  rc = check_ptrs({x, w_router, w_gate, w_up, w_down, y, workspace},
+  rc = check_ptrs({x, w_router, ex.wg, ex.wu, ex.wd, y, workspace},
                   {logit_offset, topk_ids, topk_weights, expert_counts});
   if (rc) return rc;
+  if (ex.sg && (rc = check_ptrs({ex.sg, ex.su, ex.sd}, {}))) return rc;
   const Layout L = layout(T, H, I, E, k);
   if (workspace_bytes < L.total) return BEAM_MOE_ERR_WORKSPACE_TOO_SMALL;
   int num_cu;
@@ -377,8 +437,39 @@ int beam_moe_block(void* stream, int64_t T, int H, int I, int E, int groups, int
   rc = run_route(st, T, H, E, groups, topk_groups, k, scale, x, w_router, logit_offset, ids, w,
                  nullptr, L, ws, slot);
   if (rc) return rc;
-  return run_forward(st, T, H, I, E, k, x, ids, w, w_gate, w_up, w_down, y, expert_counts, L, ws,
-                     slot, num_cu);
+  return run_forward(st, T, H, I, E, k, x, ids, w, ex, y, expert_counts, L, ws, slot, num_cu);
+}
+}  // namespace
+
+extern "C" {
+
+int beam_moe_block(void* stream, int64_t T, int H, int I, int E, int groups, int topk_groups, int k,
+                   float scale, const uint16_t* x, const uint16_t* w_router,
+                   const float* logit_offset, const uint16_t* w_gate, const uint16_t* w_up,
+                   const uint16_t* w_down, uint16_t* y, int32_t* topk_ids, float* topk_weights,
+                   int32_t* expert_counts, void* workspace, size_t workspace_bytes) {
+  const Experts ex{w_gate, w_up, w_down, nullptr, nullptr, nullptr};
+  return block_common(stream, T, H, I, E, groups, topk_groups, k, scale, x, w_router, logit_offset,
+                      ex, y, topk_ids, topk_weights, expert_counts, workspace, workspace_bytes);
+}
+
+int beam_moe_block_fp8(void* stream, int64_t T, int H, int I, int E, int groups, int topk_groups,
+                       int k, float scale, const uint16_t* x, const uint16_t* w_router,
+                       const float* logit_offset, const uint8_t* w_gate, const float* s_gate,
+                       const uint8_t* w_up, const float* s_up, const uint8_t* w_down,
+                       const float* s_down, uint16_t* y, int32_t* topk_ids, float* topk_weights,
+                       int32_t* expert_counts, void* workspace, size_t workspace_bytes) {
+  if (!s_gate || !s_up || !s_down) {
+    const int rc = check_route_dims(T, H, E, groups, topk_groups, k, scale);
+    if (rc) return rc;
+    if (check_forward_dims(T, H, I, E, k)) return BEAM_MOE_ERR_INVALID_DIM;
+    if (T == 0) return BEAM_MOE_OK;
+    return BEAM_MOE_ERR_NULL_POINTER;
+  }
+  const Experts ex{reinterpret_cast<const uint16_t*>(w_gate), reinterpret_cast<const uint16_t*>(w_up),
+                   reinterpret_cast<const uint16_t*>(w_down), s_gate, s_up, s_down};
+  return block_common(stream, T, H, I, E, groups, topk_groups, k, scale, x, w_router, logit_offset,
+                      ex, y, topk_ids, topk_weights, expert_counts, workspace, workspace_bytes);
 }
 
 int beam_moe_stream_init(void* stream, int64_t T, int H, const uint16_t* x, float* stream_out) {
@@ -445,7 +536,8 @@ int beam_moe_sublayer(void* stream, int64_t T, int H, int I, int E, int groups, 
   rc = run_route(st, T, H, E, groups, topk_groups, k, scale, xin, w_router, nullptr, ids, w, nullptr,
                  L, ws, slot);
   if (rc) return rc;
-  rc = run_forward(st, T, H, I, E, k, xin, ids, w, w_gate, w_up, w_down, yb, expert_counts, L, ws,
+  const Experts ex{w_gate, w_up, w_down, nullptr, nullptr, nullptr};
+  rc = run_forward(st, T, H, I, E, k, xin, ids, w, ex, yb, expert_counts, L, ws,
                    slot, num_cu);
   if (rc) return rc;
   BEAM_TRY(launch_residual(st, yb, stream_io, T, H, eps, step));

@@ -37,6 +37,24 @@ __device__ __forceinline__ uint4 ld16_nt(const void* p) {
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint2 ld8_nt(const void* p) {
+  const u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
+  return make_uint2(v.x, v.y);
+}
+
+// Eight FP8 (E4M3) codes, byte i = element i, -> eight bf16 (exact: every
+// E4M3 value is a bf16 value), in the 16-byte MFMA operand order.
+typedef __bf16 bf16x2 __attribute__((__vector_size__(2 * sizeof(__bf16))));
+__device__ __forceinline__ uint4 fp8x8_to_bf16x8(uint2 v) {
+  const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v.x, 1.0f, false);
+  const bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v.x, 1.0f, true);
+  const bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v.y, 1.0f, false);
+  const bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v.y, 1.0f, true);
+  return make_uint4(__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b),
+                    __builtin_bit_cast(uint32_t, c), __builtin_bit_cast(uint32_t, d));
+}
+
 // One 16x16x32 bf16 MFMA (gfx950): D = A(16x32) * B(32x16) + C.
 // Lane l supplies A row (l % 16) and B column (l % 16), each with the 8
 // k-values of its 16-byte operand; the k-slot each lane group (l / 16)

@@ -41,11 +41,17 @@ namespace beam {
 // while the current one is multiplied.  Within a step, MFMA j (0..3) takes
 // 16-byte chunk 4j+q of the row segment for lane group q; the token operand
 // uses the same k mapping.
-template <int MAT, int RB, int MT>
+//
+// W8: FP8 (E4M3) weights with per-row scales.  A step's slab is half the
+// bytes (ROWS x 128 B), read as 8-byte chunks; each MFMA operand is 8 codes
+// converted to bf16 in registers (exactly); the row scales multiply the FP32
+// accumulators in the epilogue.
+template <int MAT, int RB, int MT, bool W8>
 __global__ __launch_bounds__(256) void grouped_stream_kernel(GroupedArgs a) {
   constexpr int ROWS = MAT * RB * 16;
-  constexpr int LD = ROWS / 4;  // 16-byte loads per lane per step (4 rows per wave load)
-  __shared__ __attribute__((aligned(16))) unsigned char lds[4][ROWS * 256];
+  constexpr int LD = ROWS / 4;  // loads per lane per step (16 or 8 bytes each)
+  constexpr int RB8 = W8 ? 128 : 256;  // LDS tile bytes per row
+  __shared__ __attribute__((aligned(16))) unsigned char lds[4][ROWS * RB8];
 
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int r = lane & 15, q = lane >> 4;
@@ -64,7 +70,12 @@ __global__ __launch_bounds__(256) void grouped_stream_kernel(GroupedArgs a) {
   // k-block i%4; lane l takes row l/4 of the group and physical chunk l%4,
   // i.e. logical chunk (l%4) ^ swz(row).  f0 is a multiple of 16, so the
   // row groups never cross a 128-row block.
-  const int64_t ebytes = packed_expert_bytes(N, K);
+  // FP8: the same grid of loads with 8-byte chunks (16 rows x 32 bytes =
+  // 512 bytes per wave load), chunk c of block row j at c ^ pack8_swz(j).
+  const int64_t ebytes = W8 ? packed8_expert_bytes(N, K) : packed_expert_bytes(N, K);
+  constexpr int RBYTES = W8 ? 32 : 64;       // bytes of a packed block row
+  constexpr int CH = W8 ? 8 : 16;            // bytes of a chunk (8 k-values)
+  constexpr int64_t BLK = W8 ? kPack8BlockBytes : kPackBlockBytes;
   const int nkb = K / kPackK;
   const int rb = f0 / kPackRows, rib0 = f0 % kPackRows;
   const unsigned char* lp[LD];
@@ -73,13 +84,13 @@ __global__ __launch_bounds__(256) void grouped_stream_kernel(GroupedArgs a) {
   for (int i = 0; i < LD; ++i) {
     const int grp = i >> 2, kbl = i & 3;
     const int j = lane >> 2, pc = lane & 3;
-    const int c = pc ^ pack_swz(j);
     const int m = (grp * 16) / (RB * 16);           // matrix (gate / up) of this row group
     const int rib = rib0 + (grp * 16) % (RB * 16) + j;  // row inside the 128-row block
+    const int c = pc ^ (W8 ? pack8_swz(rib) : pack_swz(rib));
     const unsigned char* base = reinterpret_cast<const unsigned char*>(m == 0 ? a.w0 : a.w1);
-    lp[i] = base + e * ebytes + ((int64_t)(rb * nkb + kbl) * kPackRows + rib) * 64 + pc * 16;
+    lp[i] = base + e * ebytes + ((int64_t)(rb * nkb + kbl) * kPackRows + rib) * RBYTES + pc * CH;
     const int rw = grp * 16 + j;                      // row of the wave's LDS tile
-    lo[i] = rw * 256 + (((4 * kbl + c) ^ (rw & 15)) << 4);
+    lo[i] = rw * RB8 + (((4 * kbl + c) ^ (rw & 15)) * CH);
   }
 
   for (int c0 = 0; c0 < n_e; c0 += 16 * MT) {
@@ -102,11 +113,15 @@ __global__ __launch_bounds__(256) void grouped_stream_kernel(GroupedArgs a) {
         for (int j = 0; j < MT; ++j) acc[m][i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     const int nsteps = K / 128;  // K is a multiple of 64; a 64-wide tail is handled below
-    uint4 R[LD];
+    uint4 R[W8 ? 1 : LD];
+    uint2 R8[W8 ? LD : 1];
     uint4 B[2][MT][4];
     auto load_w = [&](int ks) {
 #pragma unroll
-      for (int i = 0; i < LD; ++i) R[i] = ld16_nt(lp[i] + (int64_t)ks * 4 * kPackBlockBytes);
+      for (int i = 0; i < LD; ++i) {
+        if constexpr (W8) R8[i] = ld8_nt(lp[i] + (int64_t)ks * 4 * BLK);
+        else R[i] = ld16_nt(lp[i] + (int64_t)ks * 4 * BLK);
+      }
     };
     auto load_b = [&](int buf, int ks) {
 #pragma unroll
@@ -118,7 +133,10 @@ __global__ __launch_bounds__(256) void grouped_stream_kernel(GroupedArgs a) {
     auto step = [&](int buf, int ks) {
       // slab of step ks: registers -> LDS tile, then prefetch step ks+1
 #pragma unroll
-      for (int i = 0; i < LD; ++i) st16(tile + lo[i], R[i]);
+      for (int i = 0; i < LD; ++i) {
+        if constexpr (W8) *reinterpret_cast<uint2*>(tile + lo[i]) = R8[i];
+        else st16(tile + lo[i], R[i]);
+      }
       __builtin_amdgcn_wave_barrier();
       if (ks + 1 < nsteps) {
         load_w(ks + 1);
@@ -131,7 +149,11 @@ __global__ __launch_bounds__(256) void grouped_stream_kernel(GroupedArgs a) {
 #pragma unroll
           for (int i = 0; i < RB; ++i) {
             const int rw = m * RB * 16 + i * 16 + r;
-            const uint4 av = *reinterpret_cast<const uint4*>(tile + rw * 256 + (((4 * j + q) ^ r) << 4));
+            uint4 av;
+            if constexpr (W8)
+              av = fp8x8_to_bf16x8(*reinterpret_cast<const uint2*>(tile + rw * RB8 + ((4 * j + q) ^ r) * CH));
+            else
+              av = *reinterpret_cast<const uint4*>(tile + rw * RB8 + ((4 * j + q) ^ r) * CH);
 #pragma unroll
             for (int t = 0; t < MT; ++t) acc[m][i][t] = mfma16(av, B[buf][t][j], acc[m][i][t]);
           }
@@ -167,20 +189,30 @@ __global__ __launch_bounds__(256) void grouped_stream_kernel(GroupedArgs a) {
             // k = kt + 16q + 8c: k-block kt/32 + q/2, logical chunk 2(q%2) + c
             const int rib = rib0 + 16 * i + r;
             const int kb = kt / kPackK + (q >> 1);
-            const int pc = (2 * (q & 1) + c) ^ pack_swz(r);
+            const int pc = (2 * (q & 1) + c) ^ (W8 ? pack8_swz(rib) : pack_swz(rib));
             const unsigned char* base = reinterpret_cast<const unsigned char*>(m == 0 ? a.w0 : a.w1);
-            const uint4 at = ld16(base + e * ebytes + ((int64_t)(rb * nkb + kb) * kPackRows + rib) * 64 + pc * 16);
+            const unsigned char* ap =
+                base + e * ebytes + ((int64_t)(rb * nkb + kb) * kPackRows + rib) * RBYTES + pc * CH;
+            uint4 at;
+            if constexpr (W8) at = fp8x8_to_bf16x8(*reinterpret_cast<const uint2*>(ap));
+            else at = ld16(ap);
 #pragma unroll
             for (int t = 0; t < MT; ++t) acc[m][i][t] = mfma16(at, bt[t], acc[m][i][t]);
           }
       }
     }
 
-    // Epilogue: lane holds features f0+16i+4q+c (c = 0..3) of token c0+16t+r.
+    // Epilogue: lane holds features f0+16i+4q+c (c = 0..3) of token c0+16t+r
+    // (FP8: times the features' row scales first).
 #pragma unroll
     for (int i = 0; i < RB; ++i) {
       const int f = f0 + 16 * i + 4 * q;
       if (f >= N) continue;
+      f32x4 sc0 = f32x4{1.f, 1.f, 1.f, 1.f}, sc1 = sc0;
+      if constexpr (W8) {
+        sc0 = *reinterpret_cast<const f32x4*>(a.s0 + (int64_t)e * N + f);
+        if constexpr (MAT == 2) sc1 = *reinterpret_cast<const f32x4*>(a.s1 + (int64_t)e * N + f);
+      }
 #pragma unroll
       for (int t = 0; t < MT; ++t) {
         const int tok = c0 + 16 * t + r;
@@ -189,11 +221,12 @@ __global__ __launch_bounds__(256) void grouped_stream_kernel(GroupedArgs a) {
         if constexpr (MAT == 2) {
           uint32_t p[4];
 #pragma unroll
-          for (int c = 0; c < 4; ++c) p[c] = f32_to_bf16_rne(swiglu(acc[0][i][t][c], acc[1][i][t][c]));
+          for (int c = 0; c < 4; ++c)
+            p[c] = f32_to_bf16_rne(swiglu(acc[0][i][t][c] * sc0[c], acc[1][i][t][c] * sc1[c]));
           uint2 v = make_uint2(p[0] | (p[1] << 16), p[2] | (p[3] << 16));
           *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + row * N + f) = v;
         } else {
-          *reinterpret_cast<f32x4*>(static_cast<float*>(a.out) + row * N + f) = acc[0][i][t];
+          *reinterpret_cast<f32x4*>(static_cast<float*>(a.out) + row * N + f) = acc[0][i][t] * sc0;
         }
       }
     }
@@ -209,13 +242,19 @@ static int stream_mt(int64_t T, int k, int E) {
   return 4;
 }
 
+template <int MAT, int RB, bool W8>
+static hipError_t launch_stream_w(hipStream_t st, const GroupedArgs& a, int mt) {
+  dim3 grid((a.N + 4 * RB * 16 - 1) / (4 * RB * 16), a.E), block(256);
+  if (mt == 1) hipLaunchKernelGGL((grouped_stream_kernel<MAT, RB, 1, W8>), grid, block, 0, st, a);
+  else if (mt == 2) hipLaunchKernelGGL((grouped_stream_kernel<MAT, RB, 2, W8>), grid, block, 0, st, a);
+  else hipLaunchKernelGGL((grouped_stream_kernel<MAT, RB, 4, W8>), grid, block, 0, st, a);
+  return hipGetLastError();
+}
+
+// FP8 weights are recognised by their row scales.
 template <int MAT, int RB>
 static hipError_t launch_stream(hipStream_t st, const GroupedArgs& a, int mt) {
-  dim3 grid((a.N + 4 * RB * 16 - 1) / (4 * RB * 16), a.E), block(256);
-  if (mt == 1) hipLaunchKernelGGL((grouped_stream_kernel<MAT, RB, 1>), grid, block, 0, st, a);
-  else if (mt == 2) hipLaunchKernelGGL((grouped_stream_kernel<MAT, RB, 2>), grid, block, 0, st, a);
-  else hipLaunchKernelGGL((grouped_stream_kernel<MAT, RB, 4>), grid, block, 0, st, a);
-  return hipGetLastError();
+  return a.s0 ? launch_stream_w<MAT, RB, true>(st, a, mt) : launch_stream_w<MAT, RB, false>(st, a, mt);
 }
 
 hipError_t launch_gateup_stream(hipStream_t st, const GroupedArgs& a, int64_t T, int k) {

@@ -106,11 +106,18 @@ __device__ __forceinline__ void dma16(uint32_t lds, uint32_t voff, __amdgpu_buff
 //
 // MFMA s (0..1) of a step uses 16-byte chunk 2s+g of each row for lane group
 // g = l/32 of both operands.
-template <int MAT, int BM, int STAGES, int OCC>
+//
+// W8: FP8 (E4M3) weights with per-row scales.  The weight slab of a step is
+// 8 KB (32 bytes per row, two 1 KB loads per wave), so a stage is 24 KB and
+// the ring one stage deeper; an MFMA weight operand is an 8-byte LDS read
+// converted to bf16 in registers (exactly), and the row scales multiply the
+// FP32 accumulators in the epilogue.
+template <int MAT, int BM, int STAGES, int OCC, bool W8>
 __global__ __launch_bounds__(256, OCC) void grouped_tiled_kernel(GroupedArgs a) {
   static_assert(BM == 128 || BM == 256, "tokens per tile");
+  constexpr int WB = W8 ? kWBytes / 2 : kWBytes;  // weight slab per step
   constexpr int TBytes = BM * kBK * 2;         // token slab per step
-  constexpr int Stage = kWBytes + TBytes;
+  constexpr int Stage = WB + TBytes;
   constexpr int F = (MAT == 2) ? kBW / 2 : kBW;  // output features per tile
   static_assert(STAGES >= 3 && STAGES * Stage <= 160 * 1024 / OCC - 4096, "LDS");
   __shared__ __attribute__((aligned(1024))) unsigned char ring[STAGES * Stage];
@@ -149,7 +156,8 @@ __global__ __launch_bounds__(256, OCC) void grouped_tiled_kernel(GroupedArgs a) 
   const int span = (total + 7) / 8;
   const int lo = xcd * span, hi = min(total, lo + span);
   const int nk = K / kBK;
-  const uint32_t wbytes = (uint32_t)packed_expert_bytes(N, K);  // one packed expert matrix (< 2^31)
+  const uint32_t wbytes =  // one packed expert matrix (< 2^31)
+      (uint32_t)(W8 ? packed8_expert_bytes(N, K) : packed_expert_bytes(N, K));
   const __amdgpu_buffer_rsrc_t rs_act = buf_rsrc(a.act, 0x7fffffffu);
   const uint32_t tk64 = (uint32_t)a.Tk * 64u;  // one k-block of the k-major h
   const uint32_t ring_lds = (uint32_t)(uintptr_t)(lds_void*)ring;
@@ -160,7 +168,9 @@ __global__ __launch_bounds__(256, OCC) void grouped_tiled_kernel(GroupedArgs a) 
   const int lrow = lane >> 2, lpc = lane & 3;  // DMA: row within a 16-row group, physical chunk
   const uint32_t c_rd0 = r * 64 + (rchunk(r, g) << 4);      // MFMA s = 0, row r of a block
   const uint32_t c_rd1 = r * 64 + (rchunk(r, 2 + g) << 4);  // MFMA s = 1
-  const uint32_t w_base = wave * (kWBytes / 4);              // this wave's 64 weight rows
+  const uint32_t c8_rd0 = r * 32 + ((g ^ pack8_swz(r)) << 3);        // FP8 weights, s = 0
+  const uint32_t c8_rd1 = r * 32 + (((2 + g) ^ pack8_swz(r)) << 3);  // s = 1
+  const uint32_t w_base = wave * (WB / 4);                   // this wave's 64 weight rows
 
   for (int tile = lo + slot; tile < hi; tile += per_xcd) {
     // expert: largest e with s_start[e] <= tile
@@ -217,12 +227,20 @@ __global__ __launch_bounds__(256, OCC) void grouped_tiled_kernel(GroupedArgs a) 
     const char* wexp1 = reinterpret_cast<const char*>(MAT == 2 ? a.w1 : a.w0) + (int64_t)e * wbytes;
     const __amdgpu_buffer_rsrc_t rs_w0 = buf_rsrc(wexp0, wbytes);
     const __amdgpu_buffer_rsrc_t rs_w1 = buf_rsrc(wexp1, wbytes);
-    uint32_t woff[4];
+    // FP8: load d (0, 1) copies 32 rows x 32 bytes (1 KB): gate/up rows 32w
+    // of the gate (d = 0) or up (d = 1) block; down rows 64(w%2) + 32d.
+    constexpr int WPW = W8 ? 2 : 4;  // weight loads per step and wave
+    uint32_t woff[WPW];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < WPW; ++i) {
       const int blk = (MAT == 2) ? ftile : 2 * ftile + (wave >> 1);
-      const int brow = (MAT == 2) ? 32 * wave + 16 * (i & 1) : 64 * (wave & 1) + 16 * i;
-      woff[i] = ((uint32_t)blk * (uint32_t)nk * kPackRows + (uint32_t)brow) * 64u + lane * 16u;
+      if constexpr (W8) {
+        const int brow = (MAT == 2) ? 32 * wave : 64 * (wave & 1) + 32 * i;
+        woff[i] = ((uint32_t)blk * (uint32_t)nk * kPackRows + (uint32_t)brow) * 32u + lane * 16u;
+      } else {
+        const int brow = (MAT == 2) ? 32 * wave + 16 * (i & 1) : 64 * (wave & 1) + 16 * i;
+        woff[i] = ((uint32_t)blk * (uint32_t)nk * kPackRows + (uint32_t)brow) * 64u + lane * 16u;
+      }
     }
 
     // k-loop and epilogue, specialised on the number of token blocks
@@ -232,7 +250,7 @@ __global__ __launch_bounds__(256, OCC) void grouped_tiled_kernel(GroupedArgs a) 
       // by wave w; every wave issues TPW of them (rows past the tile's last
       // token load that token again and are never read).
       constexpr int TPW = (2 * NB + 3) / 4;
-      constexpr int LPS = 4 + TPW;  // direct-to-LDS loads per step and wave
+      constexpr int LPS = WPW + TPW;  // direct-to-LDS loads per step and wave
       uint32_t toff[TPW];
 #pragma unroll
       for (int q = 0; q < TPW; ++q) {
@@ -260,12 +278,17 @@ __global__ __launch_bounds__(256, OCC) void grouped_tiled_kernel(GroupedArgs a) 
           for (int i = 0; i < 16; ++i) acc[b][j][i] = 0.f;
 
       auto dma_op = [&](int d, uint32_t st, uint32_t so) {
-        if (d < 4)  // weights: k-block kt of the packed block, so * 128 = kt * 8 KB
-          dma16(__builtin_amdgcn_readfirstlane(st + w_base + 16 * d * 64), woff[d],
-                (MAT == 2 && d >= 2) ? rs_w1 : rs_w0, so * (kPackBlockBytes / (kBK * 2)));
-        else  // tokens: x step offset kt * 64, or k-major h block kt * Tk * 64
-          dma16(__builtin_amdgcn_readfirstlane(st + kWBytes + 16 * (4 * (d - 4) + wave) * 64),
-                toff[d - 4], rs_act, (MAT == 2) ? so : (so >> 6) * tk64);
+        if (d < WPW) {  // weights: k-block kt of the packed block (so = kt * 64)
+          if constexpr (W8)
+            dma16(__builtin_amdgcn_readfirstlane(st + w_base + 1024 * d), woff[d],
+                  (MAT == 2 && d == 1) ? rs_w1 : rs_w0, so * (kPack8BlockBytes / (kBK * 2)));
+          else
+            dma16(__builtin_amdgcn_readfirstlane(st + w_base + 16 * d * 64), woff[d],
+                  (MAT == 2 && d >= 2) ? rs_w1 : rs_w0, so * (kPackBlockBytes / (kBK * 2)));
+        } else {  // tokens: x step offset kt * 64, or k-major h block kt * Tk * 64
+          dma16(__builtin_amdgcn_readfirstlane(st + WB + 16 * (4 * (d - WPW) + wave) * 64),
+                toff[d - WPW], rs_act, (MAT == 2) ? so : (so >> 6) * tk64);
+        }
       };
       auto issue = [&](int kt) {  // loads of step kt into stage kt % STAGES
         const uint32_t st = ring_lds + (kt % STAGES) * Stage;
@@ -290,11 +313,16 @@ __global__ __launch_bounds__(256, OCC) void grouped_tiled_kernel(GroupedArgs a) 
       auto read_ops = [&](const unsigned char* sb, int s, uint4 (&af)[2], uint4 (&bf)[NB]) {
         const uint32_t c = s ? c_rd1 : c_rd0;
 #pragma unroll
-        for (int b = 0; b < 2; ++b)
-          af[b] = *reinterpret_cast<const uint4*>(sb + w_base + 2048 * b + c);
+        for (int b = 0; b < 2; ++b) {
+          if constexpr (W8)
+            af[b] = fp8x8_to_bf16x8(
+                *reinterpret_cast<const uint2*>(sb + w_base + 1024 * b + (s ? c8_rd1 : c8_rd0)));
+          else
+            af[b] = *reinterpret_cast<const uint4*>(sb + w_base + 2048 * b + c);
+        }
 #pragma unroll
         for (int j = 0; j < NB; ++j)
-          bf[j] = *reinterpret_cast<const uint4*>(sb + kWBytes + 2048 * j + c);
+          bf[j] = *reinterpret_cast<const uint4*>(sb + WB + 2048 * j + c);
         __builtin_amdgcn_sched_barrier(0);  // reads go out before the MFMAs that follow
       };
 
@@ -351,10 +379,16 @@ __global__ __launch_bounds__(256, OCC) void grouped_tiled_kernel(GroupedArgs a) 
             // f..f+3 share one chunk.
             const int f = fw + 8 * q4 + 4 * g;
             if (f >= N) continue;
+            f32x4 sg = f32x4{1.f, 1.f, 1.f, 1.f}, su = sg;
+            if constexpr (W8) {  // FP8 row scales of these 4 gate and up rows
+              sg = *reinterpret_cast<const f32x4*>(a.s0 + (int64_t)e * N + f);
+              su = *reinterpret_cast<const f32x4*>(a.s1 + (int64_t)e * N + f);
+            }
             uint32_t p[4];
 #pragma unroll
             for (int c = 0; c < 4; ++c)
-              p[c] = f32_to_bf16_rne(swiglu(acc[0][j][4 * q4 + c], acc[1][j][4 * q4 + c]));
+              p[c] = f32_to_bf16_rne(
+                  swiglu(acc[0][j][4 * q4 + c] * sg[c], acc[1][j][4 * q4 + c] * su[c]));
             const int64_t off = ((int64_t)(f >> 5) * a.Tk + row) * 32 +
                                 ((((f & 31) >> 3) ^ pack_swz((int)row)) << 3) + (f & 7);
             *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + off) =
@@ -364,9 +398,11 @@ __global__ __launch_bounds__(256, OCC) void grouped_tiled_kernel(GroupedArgs a) 
             for (int b = 0; b < 2; ++b) {
               const int f = fw + 32 * b + 8 * q4 + 4 * g;
               if (f >= N) continue;
+              f32x4 sd = f32x4{1.f, 1.f, 1.f, 1.f};
+              if constexpr (W8) sd = *reinterpret_cast<const f32x4*>(a.s0 + (int64_t)e * N + f);
               *reinterpret_cast<f32x4*>(static_cast<float*>(a.out) + row * N + f) =
                   f32x4{acc[b][j][4 * q4], acc[b][j][4 * q4 + 1], acc[b][j][4 * q4 + 2],
-                        acc[b][j][4 * q4 + 3]};
+                        acc[b][j][4 * q4 + 3]} * sd;
             }
           }
         }
@@ -399,16 +435,23 @@ __global__ __launch_bounds__(256, OCC) void grouped_tiled_kernel(GroupedArgs a) 
 #define BEAM_TILED_CFG 256, 4, 1
 #endif
 
-template <int MAT, int BM, int STAGES, int OCC>
+// FP8 weights (recognised by their row scales) use a 5-stage ring of 24 KB.
+#ifndef BEAM_TILED_FP8_STAGES
+#define BEAM_TILED_FP8_STAGES 5
+#endif
+
+template <int MAT, bool W8, int BM, int STAGES, int OCC>
 static hipError_t launch_tiled_cfg(hipStream_t st, const GroupedArgs& a, int num_cu) {
   const int nwg = ((num_cu * OCC + 7) / 8) * 8;  // persistent grid, a multiple of the 8 XCDs
-  hipLaunchKernelGGL((grouped_tiled_kernel<MAT, BM, STAGES, OCC>), dim3(nwg), dim3(256), 0, st, a);
+  hipLaunchKernelGGL((grouped_tiled_kernel<MAT, BM, STAGES, OCC, W8>), dim3(nwg), dim3(256), 0, st,
+                     a);
   return hipGetLastError();
 }
 
 template <int MAT>
 static hipError_t launch_tiled(hipStream_t st, const GroupedArgs& a, int num_cu) {
-  return launch_tiled_cfg<MAT, BEAM_TILED_CFG>(st, a, num_cu);
+  if (a.s0) return launch_tiled_cfg<MAT, true, 256, BEAM_TILED_FP8_STAGES, 1>(st, a, num_cu);
+  return launch_tiled_cfg<MAT, false, BEAM_TILED_CFG>(st, a, num_cu);
 }
 
 hipError_t launch_gateup_tiled(hipStream_t st, const GroupedArgs& a, int num_cu) {

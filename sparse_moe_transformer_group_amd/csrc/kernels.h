@@ -43,13 +43,29 @@ __host__ __device__ inline int64_t packed_expert_bytes(int N, int K) {
 }
 hipError_t launch_pack(hipStream_t s, const uint16_t* src, uint16_t* dst, int E, int N, int K);
 
+// FP8 (OCP E4M3) expert weights: the same block grid with one byte per
+// weight, i.e. blocks of 128 rows x 32 k = 4 KB; row j takes 32 bytes and
+// its logical 8-byte chunk c (k = 32 kb + 8c .. + 7) sits at chunk position
+// c ^ pack8_swz(j).  Each row r has a scale 2^e_r (fp32, [E][N]): the
+// smallest power of two with max|W[r,:]| <= 448 * 2^e_r; a code is the E4M3
+// value nearest to W * 2^-e_r (ties to even); the weight is value * 2^e_r.
+constexpr int kPack8BlockBytes = kPackRows * kPackK;
+__host__ __device__ inline int pack8_swz(int row) { return (row >> 3) & 3; }
+__host__ __device__ inline int64_t packed8_expert_bytes(int N, int K) {
+  return (int64_t)((N + kPackRows - 1) / kPackRows) * (K / kPackK) * kPack8BlockBytes;
+}
+hipError_t launch_pack_fp8(hipStream_t s, const uint16_t* src, uint8_t* dst, float* scales, int E,
+                           int N, int K);
+
 // ---- grouped expert GEMMs (gemm_stream.hip, gemm_tiled.hip) ----
 struct GroupedArgs {
   const uint16_t* act;          // activations: x [T,H] (gate/up) or h (down): [Tk,I] row-major
                                 // on the stream path, k-major on the tiled path (see gemm_tiled.hip)
   const int32_t* sorted_tokens; // row indirection for x (gate/up); NULL for h
-  const uint16_t* w0;           // packed gate [E,I,H] or down [E,H,I]
+  const uint16_t* w0;           // packed gate [E,I,H] or down [E,H,I] (bf16, or FP8 bytes)
   const uint16_t* w1;           // packed up [E,I,H] or NULL
+  const float* s0;              // FP8 row scales of w0 [E][N], NULL for bf16 weights
+  const float* s1;              // FP8 row scales of w1, or NULL
   const int32_t* counts;        // [E]
   const int32_t* offsets;       // [E+1]
   void* out;                    // h bf16 (layout as for act) or o [Tk,H] fp32
