@@ -50,6 +50,9 @@ def parse():
                    choices=["decode", "verify", "prefill", "skewed", "stack", "tiny"])
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-sample-tokens", type=int, default=None)
+    p.add_argument("--weights", default="bf16", choices=["bf16", "fp8"],
+                   help="expert weight format: bf16 (the headline), or FP8 E4M3 with per-row "
+                        "scales (bf16 activations)")
     p.add_argument("--copy-probe", action="store_true",
                    help="also run one 1 GiB device copy (HBM counter calibration)")
     return p.parse_args()
@@ -100,7 +103,7 @@ def main():
     for l in range(layers):
         wr.append(MI.make_router(E, H, layer=l).to(dev))
         g, u, d = MI.make_expert_weights(E, H, I, dev, layer=l)
-        pk.append(bm.pack_experts(g, u, d))
+        pk.append(bm.pack_experts_fp8(g, u, d) if args.weights == "fp8" else bm.pack_experts(g, u, d))
         if l == 0:
             wg0, wu0, wd0 = g, u, d
         del g, u, d
@@ -157,7 +160,10 @@ def main():
 
     # ---- algorithmic work (per step)
     flops_step = layers * T * (2 * H * E + k * 6 * H * I)
-    bytes_step = sum(2 * (a * 3 * H * I) + 2 * E * H + 2 * T * H + 2 * T * H + 8 * T * k for a in active)
+    wbytes = 1 if args.weights == "fp8" else 2   # bytes per expert weight
+    sbytes = (lambda a: a * 4 * (2 * I + H)) if args.weights == "fp8" else (lambda a: 0)  # row scales
+    bytes_step = sum(wbytes * (a * 3 * H * I) + sbytes(a) + 2 * E * H + 2 * T * H + 2 * T * H + 8 * T * k
+                     for a in active)
     tokens_per_s = T * steps / elapsed
     tflops = flops_step / (ms_step * 1e-3) / 1e12
     gbs = bytes_step / (ms_step * 1e-3) / 1e9
@@ -165,7 +171,7 @@ def main():
     # ---- dominant kernel: gate/up GEMM + SwiGLU
     gu_ms = stage_ms["gateup"]
     a_mean = sum(active) / len(active)
-    gu_bytes = a_mean * 2 * I * H * 2 + T * H * 2 + T * k * I * 2
+    gu_bytes = a_mean * 2 * I * H * wbytes + T * H * 2 + T * k * I * 2
     gu_flops = T * k * 4 * H * I
     hbm_bound = (gu_flops / gu_bytes) < (PEAK_BF16_TFLOPS / PEAK_HBM_GBS * 1e3)
     if hbm_bound:
@@ -177,7 +183,8 @@ def main():
         roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4)}
     schedule = "stream" if T * k < 20 * E else "tiled"
-    roof["traffic"] = measured_traffic(args.workload, schedule)
+    roof["traffic"] = measured_traffic(args.workload + ("_fp8" if args.weights == "fp8" else ""),
+                                       schedule)
     roof["kernel"] = "grouped_stream_kernel<2,1,*> (gate/up)" if schedule == "stream" else \
         "grouped_tiled_kernel<2,...> (gate/up)"
     roof["algorithmic_per_launch"] = {"bytes": int(gu_bytes), "flops": int(gu_flops)}
@@ -203,9 +210,10 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "bf16" if args.weights == "bf16" else "fp8-e4m3 weights x bf16 activations",
         "data": "synthetic",
-        "config": {"workload": f"beam_moe_{args.workload}", "T": T, "H": H, "I": I, "E": E,
+        "config": {"workload": f"beam_moe_{args.workload}", "weights": args.weights,
+                   "T": T, "H": H, "I": I, "E": E,
                    "groups": shape.groups, "topk_groups": shape.topk_groups, "k": k,
                    "scale": shape.scale, "layers": layers,
                    "logit_offset": shape.offset, "active_experts": active},
@@ -219,6 +227,8 @@ def main():
 
     # ---- CPU oracle baseline on a bounded sample
     if not args.no_cpu_baseline:
+        print(f"[bench] timed loop done ({ms_step:.3f} ms/step); CPU oracle baseline next",
+              file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(args, shape, x, wr[0], wg0, wu0, wd0, off)
     print(json.dumps(out), flush=True)
 
@@ -231,6 +241,8 @@ def cpu_baseline(args, shape, x, wr, wg, wu, wd, off):
     from moe_inputs import bf16_bits
 
     n = args.cpu_sample_tokens or {"decode": 64, "tiny": 128}.get(args.workload, 16)
+    if args.weights == "fp8" and not args.cpu_sample_tokens:
+        n = 8  # the oracle's host-side E4M3 encoding of each touched expert is slow
     n = min(n, shape.T)
     xb = bf16_bits(x[:n])
     wrb = bf16_bits(wr)
@@ -240,6 +252,8 @@ def cpu_baseline(args, shape, x, wr, wg, wu, wd, off):
     ids, _, _, _ = O.group_limited_topk(O.sigmoid(z), shape.groups, shape.topk_groups, shape.k,
                                         shape.scale)
     host = {int(e): (bf16_bits(wg[e]), bf16_bits(wu[e]), bf16_bits(wd[e])) for e in np.unique(ids)}
+    if args.weights == "fp8":  # the oracle's own E4M3 encoding, dequantised (not timed)
+        host = {e: tuple(O.dequantize_rows(*O.quantize_rows(m)) for m in ws) for e, ws in host.items()}
     t0 = time.perf_counter()
     O.moe_block(xb, wrb, lambda e: host[e], shape.groups, shape.topk_groups, shape.k, shape.scale,
                 offn)
