@@ -55,7 +55,7 @@ int check_ptrs(std::initializer_list<const void*> required, std::initializer_lis
 size_t align256(size_t b) { return (b + 255) & ~size_t(255); }
 
 struct Layout {
-  size_t zpart, ids, w, counts, offsets, hist, base, sorted, rowof, h, o, xin, y, total;
+  size_t zpart, ids, w, counts, offsets, hist, base, sorted, rowof, h, o, xin, y, tctr, total;
   int S;
 };
 
@@ -102,6 +102,7 @@ Layout layout(int64_t T, int H, int I, int E, int k) {
   L.o = take(Tk * (size_t)H * 4);
   L.xin = take((size_t)T * H * 2);
   L.y = take((size_t)T * H * 2);
+  L.tctr = take(16 * 4);  // tile-claim counters: 8 for gate/up, 8 for down
   L.total = off;
   return L;
 }
@@ -244,14 +245,16 @@ int run_forward(hipStream_t st, int64_t T, int H, int I, int E, int k, const uin
     if (rc) return rc;
   }
   const bool stream = use_stream(T, H, I, k, E);
+  int32_t* tctr = reinterpret_cast<int32_t*>(ws + L.tctr);
   {
     StageScope sc(slot, ST_GATEUP, st);
-    GroupedArgs a{x, sorted, ex.wg, ex.wu, ex.sg, ex.su, counts, offsets, h, I, H, E, Tk};
+    if (!stream) BEAM_TRY(launch_fill_i32(st, tctr, 16, 0));  // a kernel, not a memset: graph-safe
+    GroupedArgs a{x, sorted, ex.wg, ex.wu, ex.sg, ex.su, counts, offsets, h, I, H, E, Tk, tctr};
     BEAM_TRY(stream ? launch_gateup_stream(st, a, T, k) : launch_gateup_tiled(st, a, num_cu));
   }
   {
     StageScope sc(slot, ST_DOWN, st);
-    GroupedArgs a{h, nullptr, ex.wd, nullptr, ex.sd, nullptr, counts, offsets, o, H, I, E, Tk};
+    GroupedArgs a{h, nullptr, ex.wd, nullptr, ex.sd, nullptr, counts, offsets, o, H, I, E, Tk, tctr + 8};
     BEAM_TRY(stream ? launch_down_stream(st, a, T, k) : launch_down_tiled(st, a, num_cu));
   }
   {

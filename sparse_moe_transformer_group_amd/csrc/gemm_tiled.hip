@@ -35,6 +35,27 @@ __device__ __forceinline__ f32x16 mfma32(uint4 a, uint4 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
 }
 
+// The same MFMA with its accumulator pinned to 16 architectural VGPRs.  A
+// wave has 256 accumulation registers (AGPRs); a tile of 320 tokens needs 320
+// accumulators per lane, so token blocks 8 and 9 accumulate in VGPRs through
+// the VGPR form of the instruction.  (Left to itself the register allocator
+// shuttles accumulators between the two files every k-step.)  The compiler
+// does not see the MFMA behind the asm, so the caller covers the hazards it
+// would have covered: no VALU write of an operand right before it (operands
+// come from LDS reads or from conversions that precede a run of builtin
+// MFMAs) and a wait-state pad before any VALU read of the result.
+typedef unsigned int u32x4e __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ f32x16 mfma32_vacc(uint4 a, uint4 b, f32x16 c) {
+  const u32x4e av = __builtin_bit_cast(u32x4e, a), bv = __builtin_bit_cast(u32x4e, b);
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(c) : "v"(av), "v"(bv));
+  return c;
+}
+// Wait states between the last VGPR-accumulator MFMA and a VALU read of its
+// result (more than the 8-pass XDL write -> VALU read requirement).
+__device__ __forceinline__ void mfma_vacc_drain(f32x16& c) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(c));
+}
+
 constexpr int kMaxE = 512;
 constexpr int kBW = 256;                 // weight rows per tile (8 MFMA row blocks of 32)
 constexpr int kBK = 32;                  // k per pipeline step (64 bytes per row)
@@ -82,7 +103,7 @@ __device__ __forceinline__ void dma16(uint32_t lds, uint32_t voff, __amdgpu_buff
     __builtin_amdgcn_sched_barrier(0);                                          \
   } while (0)
 
-// Workgroup tile: 256 weight rows x up to 256 tokens of one expert, 4 waves.
+// Workgroup tile: 256 weight rows x up to BM = 320 tokens of one expert, 4 waves.
 // Wave w owns 64 weight rows and every token of the tile, so the MFMA work
 // of a tile is proportional to its token blocks (32 tokens each) and equal on
 // the 4 SIMDs:
@@ -90,10 +111,15 @@ __device__ __forceinline__ void dma16(uint32_t lds, uint32_t voff, __amdgpu_buff
 //     (block 1) of features [f0 + 32w, f0 + 32w + 32), so SiLU(g)*u pairs sit
 //     in one lane; a tile covers 128 features;
 //   down (MAT = 1): rows [f0 + 64w, f0 + 64w + 64); a tile covers 256.
-// Accumulators: 2 x NB blocks of 32x32 FP32 (NB = token blocks, 1..8).
+// Accumulators: 2 x NB blocks of 32x32 FP32 (NB = token blocks, 1..10);
+// blocks 0..7 in AGPRs, blocks 8 and 9 in VGPRs.  320 tokens cover every
+// expert of a near-uniform 8192-token batch (200 to 300 tokens each) with
+// one tile, so no expert's weights are streamed into two CUs: what bounds
+// this kernel is the rate at which one CU's direct-to-LDS loads complete,
+// and two half-full tiles move 1.4x the bytes of one full tile per FLOP.
 //
 // At prefill sizes an expert's weights feed only ~256 tokens, about 256
-// FLOP per weight byte -- below MI355X's MFMA/HBM ridge -- so the tile is
+// FLOP per weight byte -- near MI355X's MFMA/HBM ridge -- so the tile is
 // built to keep HBM busy.  Each k-step (32 wide) moves the 16 KB weight slab
 // and the tile's token slab (64 bytes per token) straight into an LDS ring of
 // STAGES stages with direct-to-LDS buffer loads -- no vector registers are
@@ -108,13 +134,13 @@ __device__ __forceinline__ void dma16(uint32_t lds, uint32_t voff, __amdgpu_buff
 // g = l/32 of both operands.
 //
 // W8: FP8 (E4M3) weights with per-row scales.  The weight slab of a step is
-// 8 KB (32 bytes per row, two 1 KB loads per wave), so a stage is 24 KB and
+// 8 KB (32 bytes per row, two 1 KB loads per wave), so a stage is 28 KB and
 // the ring one stage deeper; an MFMA weight operand is an 8-byte LDS read
 // converted to bf16 in registers (exactly), and the row scales multiply the
 // FP32 accumulators in the epilogue.
 template <int MAT, int BM, int STAGES, int OCC, bool W8>
 __global__ __launch_bounds__(256, OCC) void grouped_tiled_kernel(GroupedArgs a) {
-  static_assert(BM == 128 || BM == 256, "tokens per tile");
+  static_assert(BM == 256 || BM == 320, "tokens per tile");
   constexpr int WB = W8 ? kWBytes / 2 : kWBytes;  // weight slab per step
   constexpr int TBytes = BM * kBK * 2;         // token slab per step
   constexpr int Stage = WB + TBytes;
@@ -172,7 +198,25 @@ __global__ __launch_bounds__(256, OCC) void grouped_tiled_kernel(GroupedArgs a) 
   const uint32_t c8_rd1 = r * 32 + (((2 + g) ^ pack8_swz(r)) << 3);  // s = 1
   const uint32_t w_base = wave * (WB / 4);                   // this wave's 64 weight rows
 
-  for (int tile = lo + slot; tile < hi; tile += per_xcd) {
+  // Tiles of an XCD's range go to its workgroups in order.  With a claim
+  // counter (one per XCD, zero at launch) each workgroup takes the next
+  // unclaimed tile when it starts one, so the 32 CUs of an XCD always work on
+  // neighbouring tiles -- the feature tiles of one expert, which read the
+  // same token slab -- however unequal the tiles are; without one, workgroup
+  // `slot` takes every per_xcd-th tile.  The next tile is claimed at the start
+  // of the current one, hiding the atomic's latency.
+  int* const ctr = a.tile_ctr ? a.tile_ctr + xcd : nullptr;
+  __shared__ int s_tile;
+  int tile = lo + slot;
+  if (ctr) {
+    if (tid == 0) s_tile = lo + __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    tile = __builtin_amdgcn_readfirstlane(s_tile);
+  }
+  while (tile < hi) {
+    int next = tile + per_xcd;
+    if (ctr && tid == 0)
+      next = lo + __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     // expert: largest e with s_start[e] <= tile
     int elo = 0, ehi = E - 1;
     while (elo < ehi) {
@@ -276,6 +320,16 @@ __global__ __launch_bounds__(256, OCC) void grouped_tiled_kernel(GroupedArgs a) 
         for (int j = 0; j < NB; ++j)
 #pragma unroll
           for (int i = 0; i < 16; ++i) acc[b][j][i] = 0.f;
+      // VGPR accumulators: materialise the zeros, then pad the VALU write ->
+      // MFMA srcC read before the first asm MFMA (volatile asm keeps order)
+      if constexpr (NB > 8) {
+#pragma unroll
+        for (int j = 8; j < NB; ++j) {
+          asm volatile("" : "+v"(acc[0][j]));
+          asm volatile("" : "+v"(acc[1][j]));
+        }
+        asm volatile("s_nop 4");
+      }
 
       auto dma_op = [&](int d, uint32_t st, uint32_t so) {
         if (d < WPW) {  // weights: k-block kt of the packed block (so = kt * 64)
@@ -343,7 +397,10 @@ __global__ __launch_bounds__(256, OCC) void grouped_tiled_kernel(GroupedArgs a) 
           int d = 0;
 #pragma unroll
           for (int m = 0; m < NM; ++m) {
-            acc[m & 1][m >> 1] = mfma32(af0[m & 1], bf0[m >> 1], acc[m & 1][m >> 1]);
+            if ((m >> 1) >= 8)
+              acc[m & 1][m >> 1] = mfma32_vacc(af0[m & 1], bf0[m >> 1], acc[m & 1][m >> 1]);
+            else
+              acc[m & 1][m >> 1] = mfma32(af0[m & 1], bf0[m >> 1], acc[m & 1][m >> 1]);
             if (m % EVERY == EVERY - 1 && d < LPS) {
               dma_op(d, st, so);
               ++d;
@@ -359,10 +416,19 @@ __global__ __launch_bounds__(256, OCC) void grouped_tiled_kernel(GroupedArgs a) 
         // next step's first operands (after the last step: a stale stage, unused)
         read_ops(ring + ((kt + 1) % STAGES) * Stage, 0, af0, bf0);
 #pragma unroll
-        for (int m = 0; m < 2 * NB; ++m)
-          acc[m & 1][m >> 1] = mfma32(af1[m & 1], bf1[m >> 1], acc[m & 1][m >> 1]);
+        for (int m = 0; m < 2 * NB; ++m) {
+          if ((m >> 1) >= 8)
+            acc[m & 1][m >> 1] = mfma32_vacc(af1[m & 1], bf1[m >> 1], acc[m & 1][m >> 1]);
+          else
+            acc[m & 1][m >> 1] = mfma32(af1[m & 1], bf1[m >> 1], acc[m & 1][m >> 1]);
+        }
       }
       BEAM_STEP_BARRIER(0);  // drain the clamped prefetches; the next tile may refill the ring
+#pragma unroll
+      for (int j = 8; j < NB; ++j) {
+        mfma_vacc_drain(acc[0][j]);
+        mfma_vacc_drain(acc[1][j]);
+      }
 
       // Epilogue: acc[b][j][i] is row 8*(i/4) + 4*g + (i%4) of this wave's
       // weight block b, token m0 + 32*j + r.
@@ -408,7 +474,20 @@ __global__ __launch_bounds__(256, OCC) void grouped_tiled_kernel(GroupedArgs a) 
         }
       }
     };  // run
-    if constexpr (BM == 256) {
+    if constexpr (BM == 320) {
+      switch (nb) {
+        case 1: run(std::integral_constant<int, 1>{}); break;
+        case 2: run(std::integral_constant<int, 2>{}); break;
+        case 3: run(std::integral_constant<int, 3>{}); break;
+        case 4: run(std::integral_constant<int, 4>{}); break;
+        case 5: run(std::integral_constant<int, 5>{}); break;
+        case 6: run(std::integral_constant<int, 6>{}); break;
+        case 7: run(std::integral_constant<int, 7>{}); break;
+        case 8: run(std::integral_constant<int, 8>{}); break;
+        case 9: run(std::integral_constant<int, 9>{}); break;
+        default: run(std::integral_constant<int, 10>{}); break;
+      }
+    } else {
       switch (nb) {
         case 1: run(std::integral_constant<int, 1>{}); break;
         case 2: run(std::integral_constant<int, 2>{}); break;
@@ -419,23 +498,27 @@ __global__ __launch_bounds__(256, OCC) void grouped_tiled_kernel(GroupedArgs a) 
         case 7: run(std::integral_constant<int, 7>{}); break;
         default: run(std::integral_constant<int, 8>{}); break;
       }
-    } else {
-      switch (nb) {
-        case 1: run(std::integral_constant<int, 1>{}); break;
-        case 2: run(std::integral_constant<int, 2>{}); break;
-        case 3: run(std::integral_constant<int, 3>{}); break;
-        default: run(std::integral_constant<int, 4>{}); break;
-      }
     }
+    if (ctr) {  // hand thread 0's claim to the workgroup (LDS only: the h stores may stay in flight)
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      __builtin_amdgcn_s_barrier();  // every wave has read s_tile of this tile
+      asm volatile("" ::: "memory");
+      if (tid == 0) s_tile = next;
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      next = s_tile;
+    }
+    tile = __builtin_amdgcn_readfirstlane(next);
   }
 }
 
 // Tile configuration: tokens per tile, ring depth, workgroups per CU.
 #ifndef BEAM_TILED_CFG
-#define BEAM_TILED_CFG 256, 4, 1
+#define BEAM_TILED_CFG 320, 4, 1
 #endif
 
-// FP8 weights (recognised by their row scales) use a 5-stage ring of 24 KB.
+// FP8 weights (recognised by their row scales) use a 5-stage ring of 28 KB.
 #ifndef BEAM_TILED_FP8_STAGES
 #define BEAM_TILED_FP8_STAGES 5
 #endif
@@ -450,7 +533,7 @@ static hipError_t launch_tiled_cfg(hipStream_t st, const GroupedArgs& a, int num
 
 template <int MAT>
 static hipError_t launch_tiled(hipStream_t st, const GroupedArgs& a, int num_cu) {
-  if (a.s0) return launch_tiled_cfg<MAT, true, 256, BEAM_TILED_FP8_STAGES, 1>(st, a, num_cu);
+  if (a.s0) return launch_tiled_cfg<MAT, true, 320, BEAM_TILED_FP8_STAGES, 1>(st, a, num_cu);
   return launch_tiled_cfg<MAT, false, BEAM_TILED_CFG>(st, a, num_cu);
 }
 

@@ -73,6 +73,8 @@ struct GroupedArgs {
   int K;                        // reduction length (H or I)
   int E;
   int64_t Tk;                   // number of assignments (rows of h / o)
+  int* tile_ctr;                // tiled schedule: 8 per-XCD tile-claim counters, zero at
+                                // launch (NULL: static round-robin); unused by the stream path
 };
 // Decode-size batches: every weight row is streamed once per <= 16*mt tokens.
 hipError_t launch_gateup_stream(hipStream_t s, const GroupedArgs& a, int64_t T, int k);
