@@ -45,7 +45,9 @@ def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=None)
-    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--warmup", type=int, default=None,
+                   help="untimed warm-up steps (default: at least 5 and at least 0.3 s of work, "
+                        "so the timed steps run at settled clocks)")
     p.add_argument("--workload", default="decode",
                    choices=["decode", "verify", "prefill", "skewed", "stack", "tiny"])
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -74,6 +76,20 @@ def measured_traffic(workload, schedule):
     if d.get("gemm_source_sha256_16") != kernel_hash(schedule):
         return None
     return d.get("bytes_per_launch")
+
+
+def measured_clock(workload, schedule):
+    """Shader clock and MFMA-busy share of the gate/up kernel from the committed
+    counter summary (GRBM_GUI_ACTIVE, MfmaUtil), if taken on this kernel source."""
+    path = os.path.join(ROOT, "profiles", f"clock_gateup_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        d = json.load(f)
+    if d.get("gemm_source_sha256_16") != kernel_hash(schedule):
+        return None
+    return {"clock_GHz": d.get("clock_GHz"), "mfma_busy_pct": d.get("MfmaUtil_pct_mean"),
+            "bf16_mfma_peak_at_clock_TFLOPs": d.get("bf16_mfma_peak_at_this_clock_TFLOPs")}
 
 
 def main():
@@ -142,8 +158,19 @@ def main():
             active.append(int((c > 0).sum().item()))
         del tmp
 
-    for _ in range(args.warmup):
-        step()
+    if args.warmup is None:
+        # the shader clock settles over ~0.1-0.3 s of sustained load
+        torch.cuda.synchronize()
+        t_w, n_w = time.perf_counter(), 0
+        while n_w < 5 or time.perf_counter() - t_w < 0.3:
+            step()
+            n_w += 1
+            if n_w % 5 == 0:
+                torch.cuda.synchronize()
+        args.warmup = n_w
+    else:
+        for _ in range(args.warmup):
+            step()
     torch.cuda.synchronize()
 
     # ---- timed region
@@ -185,6 +212,7 @@ def main():
     schedule = "stream" if T * k < 20 * E else "tiled"
     roof["traffic"] = measured_traffic(args.workload + ("_fp8" if args.weights == "fp8" else ""),
                                        schedule)
+    roof["clock"] = measured_clock(args.workload + ("_fp8" if args.weights == "fp8" else ""), schedule)
     roof["kernel"] = "grouped_stream_kernel<2,1,*> (gate/up)" if schedule == "stream" else \
         "grouped_tiled_kernel<2,...> (gate/up)"
     roof["algorithmic_per_launch"] = {"bytes": int(gu_bytes), "flops": int(gu_flops)}
