@@ -55,6 +55,8 @@ def parse():
     p.add_argument("--weights", default="bf16", choices=["bf16", "fp8"],
                    help="expert weight format: bf16 (the headline), or FP8 E4M3 with per-row "
                         "scales (bf16 activations)")
+    p.add_argument("--no-context", action="store_true",
+                   help="skip the dense bf16 GEMM context measurement")
     p.add_argument("--copy-probe", action="store_true",
                    help="also run one 1 GiB device copy (HBM counter calibration)")
     return p.parse_args()
@@ -174,13 +176,17 @@ def main():
     torch.cuda.synchronize()
 
     # ---- timed region
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
     with bm.StageTimer(steps * layers) as timer:
         torch.cuda.synchronize()
         t0 = time.perf_counter()
-        for _ in range(steps):
+        marks[0].record()
+        for i in range(steps):
             step()
+            marks[i + 1].record()
         torch.cuda.synchronize()
         elapsed = time.perf_counter() - t0
+    step_ms = sorted(marks[i].elapsed_time(marks[i + 1]) for i in range(steps))
     ms_step = elapsed * 1e3 / steps
     launches = timer.calls
     stage_ms = {n: v / max(launches, 1) for n, v in timer.result.items()}
@@ -227,6 +233,29 @@ def main():
         torch.cuda.synchronize()
         del a, b
 
+    context = None
+    if not args.no_context:
+        # what a dense library GEMM sustains on this machine (hipBLASLt through
+        # torch.matmul, random N(0,1) bf16 operands, 8192^3), for context
+        ga = torch.randn(8192, 8192, device=dev).to(torch.bfloat16)
+        gb = torch.randn(8192, 8192, device=dev).to(torch.bfloat16)
+        torch.cuda.synchronize()
+        tw = time.perf_counter()
+        while time.perf_counter() - tw < 0.3:
+            gc = torch.matmul(ga, gb)
+            torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(20):
+            gc = torch.matmul(ga, gb)
+        e1.record()
+        torch.cuda.synchronize()
+        gt = 2.0 * 8192 ** 3 / (e0.elapsed_time(e1) / 20 * 1e-3) / 1e12
+        context = {"dense_bf16_gemm_8192_tflops": round(gt, 1),
+                   "frac_peak_mfma": round(gt / PEAK_BF16_TFLOPS, 4),
+                   "how": "torch.matmul (hipBLASLt) on random bf16 operands, 20 runs after 0.3 s warm-up"}
+        del ga, gb, gc
+
     out = {
         "metric": METRIC,
         "value": round(tokens_per_s, 1),
@@ -235,6 +264,8 @@ def main():
         "steps": steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_step, 4),
+        "ms_per_step_median": round(step_ms[len(step_ms) // 2], 4),
+        "ms_per_step_min": round(step_ms[0], 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -251,6 +282,7 @@ def main():
         "frac_peak_hbm": round(gbs / PEAK_HBM_GBS, 4),
         "stage_ms": {n: round(v, 5) for n, v in stage_ms.items()},
         "roofline": roof,
+        "context": context,
     }
 
     # ---- CPU oracle baseline on a bounded sample

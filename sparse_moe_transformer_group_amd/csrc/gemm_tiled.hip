@@ -432,6 +432,7 @@ __global__ __launch_bounds__(256, OCC) void grouped_tiled_kernel(GroupedArgs a) 
 
       // Epilogue: acc[b][j][i] is row 8*(i/4) + 4*g + (i%4) of this wave's
       // weight block b, token m0 + 32*j + r.
+      if constexpr (MAT == 2) {
 #pragma unroll
       for (int j = 0; j < NB; ++j) {
         const int tok = m0 + 32 * j + r;
@@ -439,39 +440,70 @@ __global__ __launch_bounds__(256, OCC) void grouped_tiled_kernel(GroupedArgs a) 
         const int64_t row = row0 + tok;
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) {
-          if constexpr (MAT == 2) {
-            // h k-major: feature f of row `row` sits in k-block f/32, chunk
-            // (f%32)/8 (swizzled by the row), element f%8; the 4 features
-            // f..f+3 share one chunk.
-            const int f = fw + 8 * q4 + 4 * g;
-            if (f >= N) continue;
-            f32x4 sg = f32x4{1.f, 1.f, 1.f, 1.f}, su = sg;
-            if constexpr (W8) {  // FP8 row scales of these 4 gate and up rows
-              sg = *reinterpret_cast<const f32x4*>(a.s0 + (int64_t)e * N + f);
-              su = *reinterpret_cast<const f32x4*>(a.s1 + (int64_t)e * N + f);
-            }
-            uint32_t p[4];
+          // h k-major: feature f of row `row` sits in k-block f/32, chunk
+          // (f%32)/8 (swizzled by the row), element f%8; the 4 features
+          // f..f+3 share one chunk.
+          const int f = fw + 8 * q4 + 4 * g;
+          if (f >= N) continue;
+          f32x4 sg = f32x4{1.f, 1.f, 1.f, 1.f}, su = sg;
+          if constexpr (W8) {  // FP8 row scales of these 4 gate and up rows
+            sg = *reinterpret_cast<const f32x4*>(a.s0 + (int64_t)e * N + f);
+            su = *reinterpret_cast<const f32x4*>(a.s1 + (int64_t)e * N + f);
+          }
+          uint32_t p[4];
 #pragma unroll
-            for (int c = 0; c < 4; ++c)
-              p[c] = f32_to_bf16_rne(
-                  swiglu(acc[0][j][4 * q4 + c] * sg[c], acc[1][j][4 * q4 + c] * su[c]));
-            const int64_t off = ((int64_t)(f >> 5) * a.Tk + row) * 32 +
-                                ((((f & 31) >> 3) ^ pack_swz((int)row)) << 3) + (f & 7);
-            *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + off) =
-                make_uint2(p[0] | (p[1] << 16), p[2] | (p[3] << 16));
-          } else {
+          for (int c = 0; c < 4; ++c)
+            p[c] = f32_to_bf16_rne(
+                swiglu(acc[0][j][4 * q4 + c] * sg[c], acc[1][j][4 * q4 + c] * su[c]));
+          const int64_t off = ((int64_t)(f >> 5) * a.Tk + row) * 32 +
+                              ((((f & 31) >> 3) ^ pack_swz((int)row)) << 3) + (f & 7);
+          *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + off) =
+              make_uint2(p[0] | (p[1] << 16), p[2] | (p[3] << 16));
+        }
+      }
+      } else {
+        // Down: a tile's output row is 256 contiguous FP32 features (1 KB) per
+        // token.  Each 32-token block is staged through LDS so that one store
+        // instruction writes one whole row (64 lanes x 16 B) rather than 32
+        // rows x 32 B.  Two staging areas alternate in the idle ring, so one
+        // barrier per block keeps writers of block j+2 behind the readers of
+        // block j; rows are padded by 16 B so the column writes of a wave
+        // spread over all banks.
+        constexpr int RS = 1024 + 16;  // staging row stride, bytes
+        static_assert(2 * 32 * RS <= STAGES * Stage, "staging fits the ring");
 #pragma unroll
-            for (int b = 0; b < 2; ++b) {
-              const int f = fw + 32 * b + 8 * q4 + 4 * g;
-              if (f >= N) continue;
-              f32x4 sd = f32x4{1.f, 1.f, 1.f, 1.f};
-              if constexpr (W8) sd = *reinterpret_cast<const f32x4*>(a.s0 + (int64_t)e * N + f);
-              *reinterpret_cast<f32x4*>(static_cast<float*>(a.out) + row * N + f) =
-                  f32x4{acc[b][j][4 * q4], acc[b][j][4 * q4 + 1], acc[b][j][4 * q4 + 2],
-                        acc[b][j][4 * q4 + 3]} * sd;
+        for (int j = 0; j < NB; ++j) {
+          unsigned char* stg = ring + (j & 1) * (32 * RS);
+#pragma unroll
+          for (int b = 0; b < 2; ++b)
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+              const int fl = 64 * wave + 32 * b + 8 * q4 + 4 * g;  // feature within the tile
+              f32x4 v = f32x4{acc[b][j][4 * q4], acc[b][j][4 * q4 + 1], acc[b][j][4 * q4 + 2],
+                              acc[b][j][4 * q4 + 3]};
+              if constexpr (W8) {
+                if (fbase + fl < N) v *= *reinterpret_cast<const f32x4*>(a.s0 + (int64_t)e * N + fbase + fl);
+              }
+              *reinterpret_cast<f32x4*>(stg + r * RS + fl * 4) = v;
             }
+          asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+          __builtin_amdgcn_s_barrier();
+          asm volatile("" ::: "memory");
+          const int f = fbase + 4 * lane;
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            const int rr = 8 * wave + i;  // token of the block, wave-uniform
+            const int tok = m0 + 32 * j + rr;
+            if (tok < m1 && f < N)
+              *reinterpret_cast<f32x4*>(static_cast<float*>(a.out) + (int64_t)(row0 + tok) * N + f) =
+                  *reinterpret_cast<const f32x4*>(stg + rr * RS + lane * 16);
           }
         }
+        // every wave is done with the staging rows before the next tile's
+        // loads refill the ring
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
       }
     };  // run
     if constexpr (BM == 320) {
