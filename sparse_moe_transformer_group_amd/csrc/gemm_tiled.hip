@@ -50,6 +50,24 @@ __device__ __forceinline__ f32x16 mfma32_vacc(uint4 a, uint4 b, f32x16 c) {
   asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(c) : "v"(av), "v"(bv));
   return c;
 }
+// FP8 (E4M3) -> bf16 of 8 weights (exact), as volatile asm: volatile asm
+// keeps its place among the k-loop's other volatile asm (the direct-to-LDS
+// loads), so the conversion stays where it is put instead of being hoisted
+// next to the LDS read it waits on.  Byte 2i+h of the input is element 2i+h.
+// The trailing s_nop covers a VALU write -> MFMA operand read that follows.
+__device__ __forceinline__ uint4 fp8x8_to_bf16x8_pinned(uint2 v) {
+  uint4 o;
+  asm volatile(
+      "v_cvt_scalef32_pk_bf16_fp8 %0, %4, 1.0\n\t"
+      "v_cvt_scalef32_pk_bf16_fp8 %1, %4, 1.0 op_sel:[1,0,0]\n\t"
+      "v_cvt_scalef32_pk_bf16_fp8 %2, %5, 1.0\n\t"
+      "v_cvt_scalef32_pk_bf16_fp8 %3, %5, 1.0 op_sel:[1,0,0]\n\t"
+      "s_nop 1"
+      : "=&v"(o.x), "=&v"(o.y), "=&v"(o.z), "=&v"(o.w)
+      : "v"(v.x), "v"(v.y));
+  return o;
+}
+
 // Wait states between the last VGPR-accumulator MFMA and a VALU read of its
 // result (more than the 8-pass XDL write -> VALU read requirement).
 __device__ __forceinline__ void mfma_vacc_drain(f32x16& c) {
@@ -364,13 +382,16 @@ __global__ __launch_bounds__(256, OCC) void grouped_tiled_kernel(GroupedArgs a) 
       BEAM_STEP_BARRIER((STAGES - 2) * LPS);
 
       // Operands of MFMA s of the step whose stage starts at sb.
-      auto read_ops = [&](const unsigned char* sb, int s, uint4 (&af)[2], uint4 (&bf)[NB]) {
+      // FP8 weights: the raw 8-byte codes are read here and converted to bf16
+      // halfway through the MFMA group that precedes their use (to_bf16),
+      // so the conversion never waits on a read that was just issued.
+      auto read_ops = [&](const unsigned char* sb, int s, uint4 (&af)[2], uint2 (&ar)[2],
+                          uint4 (&bf)[NB]) {
         const uint32_t c = s ? c_rd1 : c_rd0;
 #pragma unroll
         for (int b = 0; b < 2; ++b) {
           if constexpr (W8)
-            af[b] = fp8x8_to_bf16x8(
-                *reinterpret_cast<const uint2*>(sb + w_base + 1024 * b + (s ? c8_rd1 : c8_rd0)));
+            ar[b] = *reinterpret_cast<const uint2*>(sb + w_base + 1024 * b + (s ? c8_rd1 : c8_rd0));
           else
             af[b] = *reinterpret_cast<const uint4*>(sb + w_base + 2048 * b + c);
         }
@@ -384,13 +405,23 @@ __global__ __launch_bounds__(256, OCC) void grouped_tiled_kernel(GroupedArgs a) 
       // the two MFMA groups of step kt, so the reads of the next group are
       // always in flight while the current one runs.
       uint4 af0[2], bf0[NB], af1[2], bf1[NB];
-      read_ops(ring, 0, af0, bf0);
+      uint2 ar0[2], ar1[2];
+      auto to_bf16 = [&](uint4 (&af)[2], const uint2 (&ar)[2]) {
+        if constexpr (W8) {
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int b = 0; b < 2; ++b) af[b] = fp8x8_to_bf16x8_pinned(ar[b]);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      };
+      read_ops(ring, 0, af0, ar0, bf0);
+      to_bf16(af0, ar0);
       for (int kt = 0; kt < nk; ++kt) {
         const unsigned char* sb = ring + (kt % STAGES) * Stage;
         const int ki = min(kt + STAGES - 1, nk - 1);
         const uint32_t st = ring_lds + (ki % STAGES) * Stage;
         const uint32_t so = (uint32_t)ki * (kBK * 2);
-        read_ops(sb, 1, af1, bf1);
+        read_ops(sb, 1, af1, ar1, bf1);
         {
           constexpr int NM = 2 * NB;
           constexpr int EVERY = NM / LPS > 0 ? NM / LPS : 1;
@@ -401,6 +432,7 @@ __global__ __launch_bounds__(256, OCC) void grouped_tiled_kernel(GroupedArgs a) 
               acc[m & 1][m >> 1] = mfma32_vacc(af0[m & 1], bf0[m >> 1], acc[m & 1][m >> 1]);
             else
               acc[m & 1][m >> 1] = mfma32(af0[m & 1], bf0[m >> 1], acc[m & 1][m >> 1]);
+            if (m == NM / 2 - 1) to_bf16(af1, ar1);
             if (m % EVERY == EVERY - 1 && d < LPS) {
               dma_op(d, st, so);
               ++d;
@@ -414,13 +446,14 @@ __global__ __launch_bounds__(256, OCC) void grouped_tiled_kernel(GroupedArgs a) 
         // kt are done; after the barrier, the same holds for every wave
         BEAM_STEP_BARRIER((STAGES - 2) * LPS);
         // next step's first operands (after the last step: a stale stage, unused)
-        read_ops(ring + ((kt + 1) % STAGES) * Stage, 0, af0, bf0);
+        read_ops(ring + ((kt + 1) % STAGES) * Stage, 0, af0, ar0, bf0);
 #pragma unroll
         for (int m = 0; m < 2 * NB; ++m) {
           if ((m >> 1) >= 8)
             acc[m & 1][m >> 1] = mfma32_vacc(af1[m & 1], bf1[m >> 1], acc[m & 1][m >> 1]);
           else
             acc[m & 1][m >> 1] = mfma32(af1[m & 1], bf1[m >> 1], acc[m & 1][m >> 1]);
+          if (m == NB - 1) to_bf16(af0, ar0);
         }
       }
       BEAM_STEP_BARRIER(0);  // drain the clamped prefetches; the next tile may refill the ring
