@@ -47,8 +47,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
       a3 = fmaf(wj[u], v[u][3], a3);
     }
   }
-  const uint2 pk = make_uint2(f32_to_bf16_rne(a0) | (f32_to_bf16_rne(a1) << 16),
-                              f32_to_bf16_rne(a2) | (f32_to_bf16_rne(a3) << 16));
+  const uint2 pk = make_uint2(pack_bf16x2_rne(a0, a1), pack_bf16x2_rne(a2, a3));
   *reinterpret_cast<uint2*>(y + t * H + c) = pk;
 }
 
@@ -113,8 +112,7 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const float* __restrict__ 
   for (int c = threadIdx.x * 4; c < H; c += 1024) {
     const f32x4 v = *reinterpret_cast<const f32x4*>(row + c);
     *reinterpret_cast<uint2*>(orow + c) =
-        make_uint2(f32_to_bf16_rne(v[0] * inv) | (f32_to_bf16_rne(v[1] * inv) << 16),
-                   f32_to_bf16_rne(v[2] * inv) | (f32_to_bf16_rne(v[3] * inv) << 16));
+        make_uint2(pack_bf16x2_rne(v[0] * inv, v[1] * inv), pack_bf16x2_rne(v[2] * inv, v[3] * inv));
   }
 }
 

@@ -12,16 +12,6 @@ typedef float f32x4 __attribute__((__vector_size__(4 * sizeof(float))));
 // bf16 bit pattern -> fp32 (exact).
 __device__ __forceinline__ float bf16_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
 
-// fp32 -> bf16 bit pattern, round to nearest, ties to even.  Adding 0x7fff
-// plus the lowest kept bit carries into the kept bits exactly when the
-// dropped half is above one half ulp, or equal to it with an odd kept part.
-__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;  // NaN stays NaN
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return u >> 16;
-}
-
 // 16-byte global load / store helpers.
 __device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
 __device__ __forceinline__ void st16(void* p, uint4 v) { *reinterpret_cast<uint4*>(p) = v; }
@@ -46,6 +36,16 @@ __device__ __forceinline__ uint2 ld8_nt(const void* p) {
 // Eight FP8 (E4M3) codes, byte i = element i, -> eight bf16 (exact: every
 // E4M3 value is a bf16 value), in the 16-byte MFMA operand order.
 typedef __bf16 bf16x2 __attribute__((__vector_size__(2 * sizeof(__bf16))));
+
+// Two fp32 values -> a packed bf16 pair (a in the low half), round to
+// nearest, ties to even: one v_cvt_pk_bf16_f32.  For finite inputs it gives
+// exactly the integer rounding (add 0x7fff plus the lowest kept bit, keep the
+// high half) -- checked on the device over all finite exponents, exact ties
+// and subnormals; a NaN stays a (quiet) NaN.
+__device__ __forceinline__ uint32_t pack_bf16x2_rne(float a, float b) {
+  const bf16x2 v = {(__bf16)a, (__bf16)b};
+  return __builtin_bit_cast(uint32_t, v);
+}
 __device__ __forceinline__ uint4 fp8x8_to_bf16x8(uint2 v) {
   const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v.x, 1.0f, false);
   const bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v.x, 1.0f, true);

@@ -219,11 +219,10 @@ __global__ __launch_bounds__(256) void grouped_stream_kernel(GroupedArgs a) {
         if (tok >= n_e) continue;
         const int64_t row = row0 + tok;
         if constexpr (MAT == 2) {
-          uint32_t p[4];
+          float h4[4];
 #pragma unroll
-          for (int c = 0; c < 4; ++c)
-            p[c] = f32_to_bf16_rne(swiglu(acc[0][i][t][c] * sc0[c], acc[1][i][t][c] * sc1[c]));
-          uint2 v = make_uint2(p[0] | (p[1] << 16), p[2] | (p[3] << 16));
+          for (int c = 0; c < 4; ++c) h4[c] = swiglu(acc[0][i][t][c] * sc0[c], acc[1][i][t][c] * sc1[c]);
+          uint2 v = make_uint2(pack_bf16x2_rne(h4[0], h4[1]), pack_bf16x2_rne(h4[2], h4[3]));
           *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + row * N + f) = v;
         } else {
           *reinterpret_cast<f32x4*>(static_cast<float*>(a.out) + row * N + f) = acc[0][i][t] * sc0;

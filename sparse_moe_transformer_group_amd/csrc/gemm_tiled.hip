@@ -483,15 +483,14 @@ __global__ __launch_bounds__(256, OCC) void grouped_tiled_kernel(GroupedArgs a) 
             sg = *reinterpret_cast<const f32x4*>(a.s0 + (int64_t)e * N + f);
             su = *reinterpret_cast<const f32x4*>(a.s1 + (int64_t)e * N + f);
           }
-          uint32_t p[4];
+          float h4[4];
 #pragma unroll
           for (int c = 0; c < 4; ++c)
-            p[c] = f32_to_bf16_rne(
-                swiglu(acc[0][j][4 * q4 + c] * sg[c], acc[1][j][4 * q4 + c] * su[c]));
+            h4[c] = swiglu(acc[0][j][4 * q4 + c] * sg[c], acc[1][j][4 * q4 + c] * su[c]);
           const int64_t off = ((int64_t)(f >> 5) * a.Tk + row) * 32 +
                               ((((f & 31) >> 3) ^ pack_swz((int)row)) << 3) + (f & 7);
           *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + off) =
-              make_uint2(p[0] | (p[1] << 16), p[2] | (p[3] << 16));
+              make_uint2(pack_bf16x2_rne(h4[0], h4[1]), pack_bf16x2_rne(h4[2], h4[3]));
         }
       }
       } else {
