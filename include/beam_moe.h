@@ -225,6 +225,40 @@ int beam_moe_sublayer(void* stream, int64_t T, int H, int I, int E, int groups, 
                       void* workspace, size_t workspace_bytes);
 
 /*
+ * Attention sublayer of one sequence (prefill): page "Willkommen Beam: ein
+ * offenes 501B-Modell, das Sie besitzen, anpassen und skalieren können",
+ * section "Attention" (grouped-query attention, 48 query heads and 8
+ * key/value heads, RMSNorm on queries and keys, RoPE on the sliding-window
+ * layers, the query scaling (1 + (pos + 1) / 2048)^0.1 on the global layers,
+ * a sigmoid gate from the layer input on every channel of every head before
+ * the output projection); section "Long Context" (head size 128); section
+ * "Residual Stream" (RoPE and the query scaling in FP32).
+ *
+ *   u       [T, H] bf16, the layer input at positions 0 .. T-1
+ *   w_qkvg  [Wq; Wk; Wv; Wg] stacked into one [14336, H] matrix (rows 0..6143
+ *           Wq, 6144..7167 Wk, 7168..8191 Wv, 8192..14335 Wg), packed with
+ *           beam_moe_pack_weights(E = 1, N = 14336, K = H)
+ *   w_o     Wo [H, 6144] packed with beam_moe_pack_weights(E = 1, N = H, K = 6144)
+ *   y       [T, H] bf16 out
+ *   global_layer  1: no position encoding, queries scaled; 0: RoPE with base
+ *           theta on dims (i, i + 64), keys j with i - window < j <= i
+ *
+ * Per head: q and k are RMSNorm-ed over their 128 dims (eps 1e-6, unit gain,
+ * FP32), then rotated or scaled, and rounded to bf16; v is rounded to bf16;
+ * scores are scaled by 1/sqrt(128); softmax in FP32; query head h reads
+ * key/value head h / 6; the gated head outputs are rounded to bf16 before the
+ * output projection.  Constraints: 0 <= T <= 65536, H a multiple of 64
+ * in [64, 32768], T * H < 2^30,
+ * window >= 1 and theta > 0 on sliding-window layers.  Workspace:
+ * beam_attn_workspace_bytes(T, H) bytes (0 for invalid sizes), 16-byte
+ * aligned, contents not preserved.  Errors as for the MoE calls.
+ */
+size_t beam_attn_workspace_bytes(int64_t T, int H);
+int beam_attn_forward(void* stream, int64_t T, int H, int global_layer, int window, float theta,
+                      const uint16_t* u, const uint16_t* w_qkvg, const uint16_t* w_o, uint16_t* y,
+                      void* workspace, size_t workspace_bytes);
+
+/*
  * Expert-GEMM schedule for later calls in this process: 0 = automatic (the
  * weight-streaming schedule when there are fewer than 20 assignments per
  * expert on average, the LDS-tiled schedule otherwise), 1 = always
@@ -236,7 +270,7 @@ int beam_moe_set_schedule(int mode);
 
 /*
  * Stage timer (measurement aid).  After beam_moe_timer_begin(max_calls), each
- * block / forward call (up to max_calls of them) records a hipEvent before
+ * block / forward / attention call (up to max_calls of them) records a hipEvent before
  * and after each of its stages on its stream.  beam_moe_timer_end
  * synchronises those events, writes the summed milliseconds of each stage
  * into stage_ms[0 .. n_stages-1] (n_stages >= beam_moe_stage_count()), the

@@ -12,6 +12,7 @@ besitzen, anpassen und skalieren können", sections "Attention" and
 skewed / stacked batches this repository measures.
 
 Value recipe (no trained weights exist here):
+  * attention input u ~ N(0, 1) and Wq, Wk, Wv, Wg, Wo ~ N(0, 0.02) -> bf16
   * x            ~ N(0, 1)    -> bf16 (round to nearest even)
   * router Wr    ~ N(0, 0.02) -> bf16, layout [E, H]
   * gate, up     ~ N(0, 0.02) -> bf16, layout [E, I, H]
@@ -34,6 +35,10 @@ SEED = 20261016
 
 # Tensor ids used to derive independent seeds.
 TID_X, TID_WR, TID_WG, TID_WU, TID_WD, TID_ZIPF_PERM, TID_ZIPF_CAL = range(7)
+TID_ATT_U, TID_ATT_WQ, TID_ATT_WK, TID_ATT_WV, TID_ATT_WG, TID_ATT_WO = range(7, 13)
+
+# attention: 48 query heads and 8 key/value heads of 128 dims
+ATT_Q_DIM, ATT_KV_DIM = 48 * 128, 8 * 128
 
 WEIGHT_SIGMA = 0.02
 X_SIGMA = 1.0
@@ -165,6 +170,20 @@ def make_block_inputs(shape: BlockShape, device, layer: int = 0, case: int = 0,
     if shape.offset == "zipf":
         off = load_zipf_offsets(shape.E).to(device)
     return BlockInputs(shape, x, wr, wg, wu, wd, off)
+
+
+def make_attention_input(T: int, H: int, layer: int = 0, case: int = 0) -> torch.Tensor:
+    """Normalised attention-layer input u [T, H] bf16 on the CPU, ~ N(0, 1)."""
+    return make_x(T, H, layer=layer, tid=TID_ATT_U, case=case)
+
+
+def make_attention_weights(H: int, layer: int = 0, case: int = 0):
+    """Wq [6144, H], Wk [1024, H], Wv [1024, H], Wg [6144, H], Wo [H, 6144]
+    bf16 on the CPU (nn.Linear layouts), each ~ N(0, 0.02)."""
+    shapes = ((TID_ATT_WQ, (ATT_Q_DIM, H)), (TID_ATT_WK, (ATT_KV_DIM, H)),
+              (TID_ATT_WV, (ATT_KV_DIM, H)), (TID_ATT_WG, (ATT_Q_DIM, H)),
+              (TID_ATT_WO, (H, ATT_Q_DIM)))
+    return tuple(_cpu_normal(shape, WEIGHT_SIGMA, case, layer, tid, *shape) for tid, shape in shapes)
 
 
 def bf16_bits(t: torch.Tensor) -> np.ndarray:

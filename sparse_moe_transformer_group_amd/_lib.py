@@ -66,6 +66,9 @@ def _load():
         "beam_moe_sublayer": (_c_int, [_c_vp, _c_i64, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
                                        _c_f, _c_f, _c_int, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp,
                                        _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_sz]),
+        "beam_attn_workspace_bytes": (_c_sz, [_c_i64, _c_int]),
+        "beam_attn_forward": (_c_int, [_c_vp, _c_i64, _c_int, _c_int, _c_int, _c_f, _c_vp, _c_vp,
+                                       _c_vp, _c_vp, _c_vp, _c_sz]),
         "beam_moe_set_schedule": (_c_int, [_c_int]),
         "beam_moe_stage_count": (_c_int, []),
         "beam_moe_stage_name": (ctypes.c_char_p, [_c_int]),
@@ -405,6 +408,52 @@ def sublayer(stream_io, step, w_router, w_gate, w_up, w_down, groups=8, topk_gro
                                _ptr(counts), _ptr(ws), ws.numel())
     _check("beam_moe_sublayer", rc)
     return (xin, yb, ids, w, counts) if keep_io else None
+
+
+ATTN_Q_HEADS, ATTN_KV_HEADS, ATTN_HEAD_DIM = 48, 8, 128
+ATTN_PROJ_ROWS = (2 * ATTN_Q_HEADS + 2 * ATTN_KV_HEADS) * ATTN_HEAD_DIM     # 14336
+
+
+def pack_attention_weights(wq, wk, wv, wg, wo):
+    """Packed attention weights (nn.Linear layouts, bf16): [Wq; Wk; Wv; Wg]
+    stacked into one [14336, H] matrix and Wo [H, 6144], each as one packed
+    matrix (E = 1).  Returns (w_qkvg, w_o)."""
+    H = wq.shape[1]
+    qd, kd = ATTN_Q_HEADS * ATTN_HEAD_DIM, ATTN_KV_HEADS * ATTN_HEAD_DIM
+    for name, t, shape in [("wq", wq, (qd, H)), ("wk", wk, (kd, H)), ("wv", wv, (kd, H)),
+                           ("wg", wg, (qd, H)), ("wo", wo, (H, qd))]:
+        _dev_tensor(t, name, torch.bfloat16, shape)
+    w_qkvg = pack_weights(torch.cat([wq, wk, wv, wg], dim=0).unsqueeze(0))
+    w_o = pack_weights(wo.unsqueeze(0))
+    return w_qkvg, w_o
+
+
+def attention_workspace_bytes(T: int, H: int) -> int:
+    n = lib.beam_attn_workspace_bytes(T, H)
+    if n == 0:
+        raise ValueError("dimensions break the library's rules")
+    return int(n)
+
+
+def attention(u, w_qkvg, w_o, global_layer, window=512, theta=10000.0, out=None):
+    """Attention sublayer of one sequence at positions 0..T-1 (beam_attn_forward).
+    u bf16 [T, H]; weights from pack_attention_weights.  Returns y bf16 [T, H]."""
+    T, H = u.shape
+    dev = u.device
+    _dev_tensor(u, "u", torch.bfloat16, (T, H))
+    if not (isinstance(w_qkvg, PackedMatrix) and isinstance(w_o, PackedMatrix)):
+        raise TypeError("weights must come from pack_attention_weights")
+    if (w_qkvg.E, w_qkvg.N, w_qkvg.K) != (1, ATTN_PROJ_ROWS, H) or \
+            (w_o.E, w_o.N, w_o.K) != (1, H, ATTN_Q_HEADS * ATTN_HEAD_DIM):
+        raise ValueError("packed attention weights do not match the hidden size")
+    y = out if out is not None else torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    _dev_tensor(y, "out", torch.bfloat16, (T, H))
+    ws = get_workspace(dev, attention_workspace_bytes(T, H))
+    rc = lib.beam_attn_forward(_stream(dev), T, H, int(bool(global_layer)), int(window),
+                               float(theta), _ptr(u), _ptr(w_qkvg.data), _ptr(w_o.data), _ptr(y),
+                               _ptr(ws), ws.numel())
+    _check("beam_attn_forward", rc)
+    return y
 
 
 def stage_names():

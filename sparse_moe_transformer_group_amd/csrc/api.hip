@@ -19,6 +19,7 @@ constexpr int64_t kMaxT = int64_t(1) << 24;
 constexpr int kMaxE = 512;
 constexpr int kMaxK = 32;
 constexpr int kMaxDim = 32768;
+constexpr int64_t kMaxAttnT = int64_t(1) << 16;  // 32-bit load offsets of the projections
 
 // ---------------------------------------------------------------- validation
 bool bad_dim64(int v) { return v < 64 || v > kMaxDim || (v % 64) != 0; }
@@ -107,6 +108,32 @@ Layout layout(int64_t T, int H, int I, int E, int k) {
   return L;
 }
 
+// Attention sublayer workspace (Tp = T rounded up to 128).
+struct AttnLayout {
+  size_t qkvg, qn, kn, vb, vt, o, counts, offsets, ctr, total;
+};
+AttnLayout attn_layout(int64_t T) {
+  AttnLayout L{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t at = off;
+    off += align256(bytes);
+    return at;
+  };
+  const size_t Tp = (size_t)((T + 127) / 128 * 128);
+  L.qkvg = take((size_t)T * kAttnProjRows * 4);
+  L.qn = take((size_t)kAttnQHeads * Tp * kAttnHeadDim * 2);
+  L.kn = take((size_t)kAttnKVHeads * Tp * kAttnHeadDim * 2);
+  L.vb = take((size_t)T * kAttnKVHeads * kAttnHeadDim * 2);
+  L.vt = take((size_t)kAttnKVHeads * kAttnHeadDim * Tp * 2);
+  L.o = take((size_t)T * kAttnQHeads * kAttnHeadDim * 2);
+  L.counts = take(4);
+  L.offsets = take(8);
+  L.ctr = take(32 * 4);
+  L.total = off;
+  return L;
+}
+
 // ---------------------------------------------------------------- device
 struct DevInfo {
   std::atomic<int> state{0};  // 0 unknown, 1 ok, -1 unsupported
@@ -159,8 +186,10 @@ bool use_stream(int64_t T, int H, int I, int k, int E) {
 }
 
 // ---------------------------------------------------------------- stage timer
-enum Stage { ST_LOGITS, ST_SELECT, ST_PERMUTE, ST_GATEUP, ST_DOWN, ST_COMBINE, NST };
-const char* kStageNames[NST] = {"router_logits", "select", "permute", "gateup", "down", "combine"};
+enum Stage { ST_LOGITS, ST_SELECT, ST_PERMUTE, ST_GATEUP, ST_DOWN, ST_COMBINE,
+             ST_ATT_PROJ, ST_ATT_CORE, ST_ATT_OUT, NST };
+const char* kStageNames[NST] = {"router_logits", "select", "permute", "gateup", "down", "combine",
+                                "attn_proj", "attn_core", "attn_out"};
 
 struct Timer {
   std::mutex mu;
@@ -551,6 +580,54 @@ int beam_moe_sublayer(void* stream, int64_t T, int H, int I, int E, int groups, 
 int beam_moe_set_schedule(int mode) {
   if (mode < 0 || mode > 2) return BEAM_MOE_ERR_INVALID_DIM;
   g_schedule.store(mode, std::memory_order_relaxed);
+  return BEAM_MOE_OK;
+}
+
+// the projections' 32-bit activation offsets: u [T, H] and o [T, 6144] bf16
+bool attn_bad_dims(int64_t T, int H) {
+  return T < 0 || T > kMaxAttnT || bad_dim64(H) || T * H * 2 >= (int64_t(1) << 31);
+}
+
+size_t beam_attn_workspace_bytes(int64_t T, int H) {
+  if (attn_bad_dims(T, H)) return 0;
+  return attn_layout(T).total;
+}
+
+int beam_attn_forward(void* stream, int64_t T, int H, int global_layer, int window, float theta,
+                      const uint16_t* u, const uint16_t* w_qkvg, const uint16_t* w_o, uint16_t* y,
+                      void* workspace, size_t workspace_bytes) {
+  if (attn_bad_dims(T, H)) return BEAM_MOE_ERR_INVALID_DIM;
+  if (global_layer != 0 && global_layer != 1) return BEAM_MOE_ERR_INVALID_DIM;
+  if (!global_layer && window < 1) return BEAM_MOE_ERR_INVALID_DIM;
+  if (!global_layer && !(isfinite(theta) && theta > 0.f)) return BEAM_MOE_ERR_INVALID_DIM;
+  if (T == 0) return BEAM_MOE_OK;
+  int rc = check_ptrs({u, w_qkvg, w_o, y, workspace}, {});
+  if (rc) return rc;
+  const AttnLayout L = attn_layout(T);
+  if (workspace_bytes < L.total) return BEAM_MOE_ERR_WORKSPACE_TOO_SMALL;
+  int num_cu;
+  if ((rc = device_check(&num_cu))) return rc;
+  const int slot = timer_claim();
+  char* ws = static_cast<char*>(workspace);
+  AttnArgs a{T, H, global_layer, window, theta, u, w_qkvg, w_o, y,
+             reinterpret_cast<float*>(ws + L.qkvg), reinterpret_cast<uint16_t*>(ws + L.qn),
+             reinterpret_cast<uint16_t*>(ws + L.kn), reinterpret_cast<uint16_t*>(ws + L.vb),
+             reinterpret_cast<uint16_t*>(ws + L.vt), reinterpret_cast<uint16_t*>(ws + L.o),
+             reinterpret_cast<int32_t*>(ws + L.counts), reinterpret_cast<int32_t*>(ws + L.offsets),
+             reinterpret_cast<int32_t*>(ws + L.ctr)};
+  hipStream_t st = (hipStream_t)stream;
+  {
+    StageScope sc(slot, ST_ATT_PROJ, st);
+    BEAM_TRY(launch_attn_proj(st, a, num_cu));
+  }
+  {
+    StageScope sc(slot, ST_ATT_CORE, st);
+    BEAM_TRY(launch_attn_core(st, a));
+  }
+  {
+    StageScope sc(slot, ST_ATT_OUT, st);
+    BEAM_TRY(launch_attn_out(st, a, num_cu));
+  }
   return BEAM_MOE_OK;
 }
 

@@ -1,0 +1,371 @@
+// Beam attention sublayer (prefill of one sequence) on gfx950.
+//
+// Page "Willkommen Beam: ein offenes 501B-Modell, das Sie besitzen, anpassen
+// und skalieren können", section "Attention": grouped-query attention with 48
+// query heads and 8 key/value heads, RMSNorm on queries and keys; sliding-
+// window layers (the previous 512 tokens) use RoPE, global layers use no
+// position encoding and multiply each query by (1 + (pos + 1) / 2048)^0.1; a
+// sigmoid gate computed from the layer input scales every channel of every
+// head before the output projection.  Section "Long Context" fixes the head
+// size at 128 (2 x 8 KV heads x 128 dims cached per token); section "Residual
+// Stream" puts RoPE and the query scaling in FP32.
+//
+// Path (one call of beam_attn_forward):
+//   1. qkvg = u [T, H] x [Wq; Wk; Wv; Wg]^T      plain tiled GEMM, FP32 out
+//   2. attn_prep:   per token and head, RMSNorm (FP32) of q and k, then RoPE
+//      (sliding window) or the query scaling (global); q, k -> bf16 head-major
+//      [head][T][128]; v -> bf16 [T][8*128]
+//   3. attn_vt:     v -> per kv head [128 dims][Tp keys] in FP16, scaled by a
+//      power of two (keys permuted inside each group of 16, see below), zero
+//      past T
+//   4. attn_flash:  softmax(q k^T / sqrt(128)) v per query head, causal and
+//      windowed, online softmax in FP32, PV in FP16; x sigmoid(gate) -> o bf16
+//      [T][6144]
+//   5. y = o x Wo^T                                plain tiled GEMM, bf16 out
+#include <math.h>
+
+#include "common.h"
+#include "kernels.h"
+
+namespace beam {
+
+typedef float f32x16a __attribute__((__vector_size__(16 * sizeof(float))));
+typedef _Float16 f16x8 __attribute__((__vector_size__(8 * sizeof(_Float16))));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ f32x16a mfma32a(uint4 a, uint4 b, f32x16a c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x16a mfma32h(uint4 a, uint4 b, f32x16a c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+}
+__device__ __forceinline__ uint32_t pack_f16x2_rne(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){a, b}, f16x2));
+}
+
+// The PV product runs in FP16 (11 significant bits for the probabilities
+// instead of bf16's 8).  v is bf16; multiplied by a power of two chosen per
+// kv head so that the largest |v| lands in [2^14, 2^15), every normal value
+// converts to FP16 exactly and none overflows.  vmax holds the per-head
+// maximum |v| as float bits (non-negative floats order like their bits).
+constexpr int kAttnVmaxSlot = 8;  // tile_ctr[8 .. 15]: the 8 kv heads' max |v|
+__device__ __forceinline__ float attn_v_scale(const int32_t* vmax, int g) {
+  const float m = __int_as_float(vmax[g]);
+  if (!(m > 0.f) || !isfinite(m)) return 1.f;
+  int e;
+  frexpf(m, &e);  // m = f 2^e, f in [0.5, 1)
+  return ldexpf(1.f, 15 - e);
+}
+
+// ---------------------------------------------------------------------------
+// setup: the one-"expert" row bookkeeping of the two GEMMs and their tile
+// counters (a kernel, not a memset, so the call can be graph-captured)
+__global__ void attn_setup_kernel(int T, int32_t* counts, int32_t* offsets, int32_t* ctr, int nctr) {
+  const int i = threadIdx.x;
+  if (i == 0) {
+    counts[0] = T;
+    offsets[0] = 0;
+    offsets[1] = T;
+  }
+  if (i < nctr) ctr[i] = 0;
+}
+
+// ---------------------------------------------------------------------------
+// prep: one workgroup per token (rows T .. Tp-1 are written as zeros).  Wave
+// w normalises heads w, w+4, ... (48 query heads, then 8 key heads); lane l
+// holds dims l and l+64, which is exactly a RoPE pair.
+__global__ __launch_bounds__(256) void attn_prep_kernel(const float* __restrict__ qkvg, int T,
+                                                        int global_layer, float theta,
+                                                        uint16_t* __restrict__ qn,
+                                                        uint16_t* __restrict__ kn,
+                                                        uint16_t* __restrict__ vb, int Tp,
+                                                        int32_t* __restrict__ vmax) {
+  const int t = blockIdx.x;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  constexpr int QW = kAttnQHeads * kAttnHeadDim, KW = kAttnKVHeads * kAttnHeadDim;
+  constexpr int NW = 2 * QW + 2 * KW;
+  if (t >= T) {  // padding rows of the head-major arrays
+    for (int h = wave; h < kAttnQHeads + kAttnKVHeads; h += 4) {
+      uint16_t* dst = (h < kAttnQHeads) ? qn + ((int64_t)h * Tp + t) * kAttnHeadDim
+                                        : kn + ((int64_t)(h - kAttnQHeads) * Tp + t) * kAttnHeadDim;
+      dst[lane] = 0;
+      dst[lane + 64] = 0;
+    }
+    return;
+  }
+  const float* row = qkvg + (int64_t)t * NW;
+  // rotation of pair `lane` at position t: the angle is formed and reduced in
+  // double precision (t * theta^(-lane/64) exceeds FP32 resolution at long
+  // positions), then sin/cos in FP32
+  float cs = 1.f, sn = 0.f, qs = 1.f;
+  if (global_layer) {
+    qs = powf(1.f + (float)(t + 1) / 2048.f, 0.1f);
+  } else {
+    const double ang = (double)t * pow((double)theta, -(double)lane / 64.0);
+    const double red = ang - 6.283185307179586 * floor(ang / 6.283185307179586);
+    sincosf((float)red, &sn, &cs);
+  }
+  for (int h = wave; h < kAttnQHeads + kAttnKVHeads; h += 4) {
+    const bool isq = h < kAttnQHeads;
+    const float* src = isq ? row + h * kAttnHeadDim : row + QW + (h - kAttnQHeads) * kAttnHeadDim;
+    float x1 = src[lane], x2 = src[lane + 64];
+    float ss = x1 * x1 + x2 * x2;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) ss += __shfl_xor(ss, off, 64);
+    const float inv = 1.0f / sqrtf(ss * (1.0f / kAttnHeadDim) + 1e-6f);
+    x1 *= inv;
+    x2 *= inv;
+    if (global_layer) {
+      if (isq) {
+        x1 *= qs;
+        x2 *= qs;
+      }
+    } else {
+      const float r1 = x1 * cs - x2 * sn, r2 = x2 * cs + x1 * sn;
+      x1 = r1;
+      x2 = r2;
+    }
+    uint16_t* dst = isq ? qn + ((int64_t)h * Tp + t) * kAttnHeadDim
+                        : kn + ((int64_t)(h - kAttnQHeads) * Tp + t) * kAttnHeadDim;
+    const uint32_t p = pack_bf16x2_rne(x1, x2);
+    dst[lane] = (uint16_t)(p & 0xffffu);
+    dst[lane + 64] = (uint16_t)(p >> 16);
+  }
+  // v -> bf16, row-major [T][8*128]; thread i holds dims 4i .. 4i+3, so the
+  // 32 lanes of each half-wave hold one kv head
+  {
+    const int c = threadIdx.x * 4;
+    const f32x4 v = *reinterpret_cast<const f32x4*>(row + QW + KW + c);
+    const uint2 b = make_uint2(pack_bf16x2_rne(v[0], v[1]), pack_bf16x2_rne(v[2], v[3]));
+    *reinterpret_cast<uint2*>(vb + (int64_t)t * KW + c) = b;
+    float m = fmaxf(fmaxf(fabsf(__uint_as_float(b.x << 16)), fabsf(__uint_as_float(b.x & 0xffff0000u))),
+                    fmaxf(fabsf(__uint_as_float(b.y << 16)), fabsf(__uint_as_float(b.y & 0xffff0000u))));
+#pragma unroll
+    for (int off = 16; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+    if ((threadIdx.x & 31) == 0 && m > 0.f) atomicMax(vmax + (threadIdx.x >> 5), __float_as_int(m));
+  }
+}
+
+// Key order inside each group of 16 in the transposed v: the attention
+// kernel's PV product takes, for MFMA lane group g, the keys 4g..4g+3 and
+// 8+4g..8+4g+3 of a group (the layout of its softmax registers), so keys
+// 4..7 and 8..11 trade places: then each lane group reads 8 contiguous keys.
+__device__ __forceinline__ int vt_slot(int key) {
+  const int k = key & 15;
+  const int s = (k >= 4 && k < 8) ? k + 4 : (k >= 8 && k < 12) ? k - 4 : k;
+  return (key & ~15) | s;
+}
+
+// vt[g][d][slot(t)] = FP16(v[t][g][d] * scale_g) for t < T, zero for
+// T <= t < Tp: 64 x 64 tiles through LDS.  grid (Tp/64, 8 heads x 2 dim halves).
+__global__ __launch_bounds__(256) void attn_vt_kernel(const uint16_t* __restrict__ vb, int T,
+                                                      int Tp, const int32_t* __restrict__ vmax,
+                                                      uint16_t* __restrict__ vt) {
+  __shared__ uint16_t tile[64][66];
+  const int t0 = blockIdx.x * 64;
+  const int g = blockIdx.y >> 1, d0 = (blockIdx.y & 1) * 64;
+  constexpr int KW = kAttnKVHeads * kAttnHeadDim;
+  const float scale = attn_v_scale(vmax, g);
+  for (int i = threadIdx.x; i < 64 * 64; i += 256) {
+    const int tt = i >> 6, dd = i & 63;
+    const int t = t0 + tt;
+    const float v = (t < T) ? __uint_as_float((uint32_t)vb[(int64_t)t * KW + g * kAttnHeadDim + d0 + dd] << 16)
+                            : 0.f;
+    tile[tt][dd] = __builtin_bit_cast(uint16_t, (_Float16)(v * scale));
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < 64 * 64; i += 256) {
+    const int dd = i >> 6, tt = i & 63;
+    vt[((int64_t)g * kAttnHeadDim + d0 + dd) * Tp + t0 + vt_slot(tt)] = tile[tt][dd];
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Flash attention.  grid (Tp/128 query blocks, 48 query heads), 4 waves; wave
+// w owns queries q0 + 32w .. + 31, one per MFMA column (lane l: query l%32).
+//   S^T = K Q^T:  A = 32 keys x 16 dims from LDS, B = the wave's queries from
+//     registers; element i of lane l is key 8(i/4) + 4(l/32) + i%4 of the
+//     32-key tile, query l%32 -- a query's scores sit in one lane and its
+//     partner l^32, so the softmax needs one cross-lane step.
+//   O^T = V^T P^T:  A = 32 dims x 16 keys of the scaled FP16 v^T from LDS
+//     (keys in vt_slot order), B = the lane's own probabilities as FP16.
+//     O^T's columns are queries, so the online-softmax rescale is lane-local.
+// LDS: the 64-key K tile (64 x 256 B) and v^T tile (128 x 128 B), 16-byte
+// chunks XOR-swizzled by row.
+__global__ __launch_bounds__(256) void attn_flash_kernel(const uint16_t* __restrict__ qn,
+                                                         const uint16_t* __restrict__ kn,
+                                                         const uint16_t* __restrict__ vt,
+                                                         const float* __restrict__ qkvg,
+                                                         const int32_t* __restrict__ vmax,
+                                                         int T, int Tp, int window,
+                                                         uint16_t* __restrict__ out) {
+  __shared__ __attribute__((aligned(16))) unsigned char ks[64 * 256];
+  __shared__ __attribute__((aligned(16))) unsigned char vs[128 * 128];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int r = lane & 31, g = lane >> 5;
+  const int h = blockIdx.y, kvh = h / (kAttnQHeads / kAttnKVHeads);
+  const int q0 = blockIdx.x * 128;
+  const int qi = q0 + 32 * wave + r;  // this lane's query
+  constexpr int D = kAttnHeadDim;
+  constexpr int NW = 2 * kAttnQHeads * D + 2 * kAttnKVHeads * D;
+
+  // the wave's queries as the B operand: dims 16s + 8g .. + 7 of query qi
+  uint4 qf[8];
+  {
+    const uint16_t* qp = qn + ((int64_t)h * Tp + qi) * D + 8 * g;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) qf[s] = *reinterpret_cast<const uint4*>(qp + 16 * s);
+  }
+
+  f32x16a o[4];
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) o[dt][i] = 0.f;
+  float m_run = -INFINITY, l_run = 0.f;
+  const float sc = 1.4426950408889634f / sqrtf((float)D);  // log2(e) / sqrt(D)
+
+  const int j_hi = min(q0 + 128, T);  // keys [j_lo, j_hi)
+  const int j_lo = window > 0 ? (max(0, q0 - window + 1) & ~63) : 0;
+  const uint16_t* kbase = kn + (int64_t)kvh * Tp * D;
+  const uint16_t* vbase = vt + (int64_t)kvh * D * Tp;
+
+  for (int j0 = j_lo; j0 < j_hi; j0 += 64) {
+    __syncthreads();  // every wave is done with the previous tiles
+    // K tile: thread -> key tid/4, chunks 4(tid%4) .. +3 (16 per 256-B row)
+    {
+      const int key = tid >> 2, c0 = 4 * (tid & 3);
+      const uint4* src = reinterpret_cast<const uint4*>(kbase + (int64_t)(j0 + key) * D);
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        *reinterpret_cast<uint4*>(ks + key * 256 + (((c0 + c) ^ (key & 15)) << 4)) = src[c0 + c];
+    }
+    // v^T tile: thread -> dim tid/2, chunks 4(tid%2) .. +3 (8 per 128-B row)
+    {
+      const int d = tid >> 1, c0 = 4 * (tid & 1);
+      const uint4* src = reinterpret_cast<const uint4*>(vbase + (int64_t)d * Tp + j0);
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        *reinterpret_cast<uint4*>(vs + d * 128 + (((c0 + c) ^ (d & 7)) << 4)) = src[c0 + c];
+    }
+    __syncthreads();
+
+    // S^T for the 64 keys: two 32-key tiles
+    f32x16a st[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) st[t][i] = 0.f;
+      const int key = 32 * t + r;
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        const uint4 kf = *reinterpret_cast<const uint4*>(ks + key * 256 + (((2 * s + g) ^ (key & 15)) << 4));
+        st[t] = mfma32a(kf, qf[s], st[t]);
+      }
+    }
+    // mask, scale (log2 domain), running max
+    float mx = -INFINITY;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int kj = j0 + 32 * t + 8 * (i >> 2) + 4 * g + (i & 3);
+        const bool ok = kj <= qi && kj < T && (window <= 0 || kj > qi - window);
+        const float v = ok ? st[t][i] * sc : -INFINITY;
+        st[t][i] = v;
+        mx = fmaxf(mx, v);
+      }
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    const float m_new = fmaxf(m_run, mx);
+    const float mref = (m_new == -INFINITY) ? 0.f : m_new;
+    const float alpha = exp2f(m_run - mref);
+    float sum = 0.f;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float p = exp2f(st[t][i] - mref);
+        st[t][i] = p;
+        sum += p;
+      }
+    sum += __shfl_xor(sum, 32, 64);
+    l_run = l_run * alpha + sum;
+    m_run = m_new;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) o[dt][i] *= alpha;
+
+    // O^T += V^T P^T: MFMA (t, hf) covers keys 32t + 16hf + 0..15
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        const uint4 pf = make_uint4(pack_f16x2_rne(st[t][8 * hf + 0], st[t][8 * hf + 1]),
+                                    pack_f16x2_rne(st[t][8 * hf + 2], st[t][8 * hf + 3]),
+                                    pack_f16x2_rne(st[t][8 * hf + 4], st[t][8 * hf + 5]),
+                                    pack_f16x2_rne(st[t][8 * hf + 6], st[t][8 * hf + 7]));
+        const int chunk = 4 * t + 2 * hf + g;  // 16-B chunk of the v^T row (slot order)
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) {
+          const int d = 32 * dt + r;
+          const uint4 vf = *reinterpret_cast<const uint4*>(vs + d * 128 + ((chunk ^ (d & 7)) << 4));
+          o[dt] = mfma32h(vf, pf, o[dt]);
+        }
+      }
+  }
+
+  // normalise, gate, store: o[dt][i] is dim 32dt + 8(i/4) + 4g + i%4 of query qi
+  if (qi < T) {
+    const float inv = 1.f / (l_run * attn_v_scale(vmax, kvh));  // both exact up to one rounding
+    // gate logits: columns QW + 2 KW .. of the projection output
+    const float* gl = qkvg + (int64_t)qi * NW + (kAttnQHeads + 2 * kAttnKVHeads) * D + h * D;
+    uint16_t* dst = out + (int64_t)qi * (kAttnQHeads * D) + h * D;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int d = 32 * dt + 8 * q4 + 4 * g;
+        const f32x4 z = *reinterpret_cast<const f32x4*>(gl + d);
+        float v[4];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) v[c] = o[dt][4 * q4 + c] * inv / (1.f + expf(-z[c]));
+        *reinterpret_cast<uint2*>(dst + d) = make_uint2(pack_bf16x2_rne(v[0], v[1]), pack_bf16x2_rne(v[2], v[3]));
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------
+static int attn_tp(int64_t T) { return (int)((T + 127) / 128 * 128); }
+
+// setup + 1. projections (FP32 q, k, v, gate logits)
+hipError_t launch_attn_proj(hipStream_t st, const AttnArgs& a, int num_cu) {
+  hipLaunchKernelGGL(attn_setup_kernel, dim3(1), dim3(64), 0, st, (int)a.T, a.counts, a.offsets,
+                     a.tile_ctr, 32);
+  GroupedArgs g{a.u, nullptr, a.w_qkvg, nullptr, nullptr, nullptr, a.counts, a.offsets,
+                a.qkvg, kAttnProjRows, a.H, 1, a.T, a.tile_ctr, 0};
+  return launch_plain_tiled(st, g, num_cu);
+}
+
+// 2-4. q/k norm and position, v layout, attention with the gate
+hipError_t launch_attn_core(hipStream_t st, const AttnArgs& a) {
+  const int Tp = attn_tp(a.T);
+  int32_t* vmax = a.tile_ctr + kAttnVmaxSlot;  // zeroed by attn_setup_kernel
+  hipLaunchKernelGGL(attn_prep_kernel, dim3(Tp), dim3(256), 0, st, a.qkvg, (int)a.T, a.global_layer,
+                     a.theta, a.qn, a.kn, a.vb, Tp, vmax);
+  hipLaunchKernelGGL(attn_vt_kernel, dim3(Tp / 64, 2 * kAttnKVHeads), dim3(256), 0, st, a.vb,
+                     (int)a.T, Tp, vmax, a.vt);
+  hipLaunchKernelGGL(attn_flash_kernel, dim3(Tp / 128, kAttnQHeads), dim3(256), 0, st, a.qn, a.kn,
+                     a.vt, a.qkvg, vmax, (int)a.T, Tp, a.global_layer ? 0 : a.window, a.o);
+  return hipGetLastError();
+}
+
+// 5. output projection, bf16 result
+hipError_t launch_attn_out(hipStream_t st, const AttnArgs& a, int num_cu) {
+  GroupedArgs g{a.o, nullptr, a.w_o, nullptr, nullptr, nullptr, a.counts, a.offsets,
+                a.y, a.H, kAttnQHeads * kAttnHeadDim, 1, a.T, a.tile_ctr + 16, 1};
+  return launch_plain_tiled(st, g, num_cu);
+}
+
+}  // namespace beam

@@ -128,7 +128,9 @@ __device__ __forceinline__ void dma16(uint32_t lds, uint32_t voff, __amdgpu_buff
 //   gate/up (MAT = 2): wave w holds the gate rows (block 0) and the up rows
 //     (block 1) of features [f0 + 32w, f0 + 32w + 32), so SiLU(g)*u pairs sit
 //     in one lane; a tile covers 128 features;
-//   down (MAT = 1): rows [f0 + 64w, f0 + 64w + 64); a tile covers 256.
+//   down (MAT = 1): rows [f0 + 64w, f0 + 64w + 64); a tile covers 256;
+//   plain GEMM (MAT = 0): the down layout of one weight matrix over
+//     row-major token rows (the attention projections): FP32 or bf16 out.
 // Accumulators: 2 x NB blocks of 32x32 FP32 (NB = token blocks, 1..10);
 // blocks 0..7 in AGPRs, blocks 8 and 9 in VGPRs.  320 tokens cover every
 // expert of a near-uniform 8192-token batch (200 to 300 tokens each) with
@@ -319,9 +321,10 @@ __global__ __launch_bounds__(256, OCC) void grouped_tiled_kernel(GroupedArgs a) 
         const int trow = 16 * (4 * q + wave) + lrow;
         const int tok = min(m0 + trow, m1 - 1);
         const int rr = row0 + tok;
-        if constexpr (MAT == 2) {
-          // x rows (row-major, gathered through sorted_tokens)
-          const uint32_t src = (uint32_t)a.sorted_tokens[rr];
+        if constexpr (MAT != 1) {
+          // x rows (row-major, gathered through sorted_tokens; in order when
+          // there is no indirection)
+          const uint32_t src = a.sorted_tokens ? (uint32_t)a.sorted_tokens[rr] : (uint32_t)rr;
           toff[q] = src * (uint32_t)K * 2u + (rchunk(trow, lpc) << 4);
         } else {
           // h in k-major order (written so by the gate/up epilogue): row rr
@@ -359,7 +362,7 @@ __global__ __launch_bounds__(256, OCC) void grouped_tiled_kernel(GroupedArgs a) 
                   (MAT == 2 && d >= 2) ? rs_w1 : rs_w0, so * (kPackBlockBytes / (kBK * 2)));
         } else {  // tokens: x step offset kt * 64, or k-major h block kt * Tk * 64
           dma16(__builtin_amdgcn_readfirstlane(st + WB + 16 * (4 * (d - WPW) + wave) * 64),
-                toff[d - WPW], rs_act, (MAT == 2) ? so : (so >> 6) * tk64);
+                toff[d - WPW], rs_act, (MAT != 1) ? so : (so >> 6) * tk64);
         }
       };
       auto issue = [&](int kt) {  // loads of step kt into stage kt % STAGES
@@ -526,9 +529,15 @@ __global__ __launch_bounds__(256, OCC) void grouped_tiled_kernel(GroupedArgs a) 
           for (int i = 0; i < 8; ++i) {
             const int rr = 8 * wave + i;  // token of the block, wave-uniform
             const int tok = m0 + 32 * j + rr;
-            if (tok < m1 && f < N)
-              *reinterpret_cast<f32x4*>(static_cast<float*>(a.out) + (int64_t)(row0 + tok) * N + f) =
-                  *reinterpret_cast<const f32x4*>(stg + rr * RS + lane * 16);
+            if (tok < m1 && f < N) {
+              const f32x4 v = *reinterpret_cast<const f32x4*>(stg + rr * RS + lane * 16);
+              const int64_t at = (int64_t)(row0 + tok) * N + f;
+              if (a.out_bf16)  // plain GEMM with a bf16 result (one RNE per value)
+                *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + at) =
+                    make_uint2(pack_bf16x2_rne(v[0], v[1]), pack_bf16x2_rne(v[2], v[3]));
+              else
+                *reinterpret_cast<f32x4*>(static_cast<float*>(a.out) + at) = v;
+            }
           }
         }
         // every wave is done with the staging rows before the next tile's
@@ -607,6 +616,10 @@ hipError_t launch_gateup_tiled(hipStream_t st, const GroupedArgs& a, int num_cu)
 
 hipError_t launch_down_tiled(hipStream_t st, const GroupedArgs& a, int num_cu) {
   return launch_tiled<1>(st, a, num_cu);
+}
+
+hipError_t launch_plain_tiled(hipStream_t st, const GroupedArgs& a, int num_cu) {
+  return launch_tiled_cfg<0, false, BEAM_TILED_CFG>(st, a, num_cu);
 }
 
 }  // namespace beam

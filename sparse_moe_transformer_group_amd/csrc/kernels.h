@@ -75,6 +75,7 @@ struct GroupedArgs {
   int64_t Tk;                   // number of assignments (rows of h / o)
   int* tile_ctr;                // tiled schedule: 8 per-XCD tile-claim counters, zero at
                                 // launch (NULL: static round-robin); unused by the stream path
+  int out_bf16;                 // plain tiled GEMM only: 1 = bf16 result, 0 = FP32
 };
 // Decode-size batches: every weight row is streamed once per <= 16*mt tokens.
 hipError_t launch_gateup_stream(hipStream_t s, const GroupedArgs& a, int64_t T, int k);
@@ -82,6 +83,37 @@ hipError_t launch_down_stream(hipStream_t s, const GroupedArgs& a, int64_t T, in
 // Prefill-size batches: LDS-staged tiles on MFMA, persistent XCD-aware schedule.
 hipError_t launch_gateup_tiled(hipStream_t s, const GroupedArgs& a, int num_cu);
 hipError_t launch_down_tiled(hipStream_t s, const GroupedArgs& a, int num_cu);
+// ---- attention sublayer (attention.hip) ----
+constexpr int kAttnQHeads = 48, kAttnKVHeads = 8, kAttnHeadDim = 128;
+constexpr int kAttnProjRows = 2 * kAttnQHeads * kAttnHeadDim + 2 * kAttnKVHeads * kAttnHeadDim;  // q,k,v,gate
+struct AttnArgs {
+  int64_t T;
+  int H;
+  int global_layer;             // 1: no RoPE, query scaling; 0: RoPE, sliding window
+  int window;                   // keys j with i - window < j <= i (sliding-window layers)
+  float theta;                  // RoPE base
+  const uint16_t* u;            // [T, H] bf16 layer input
+  const uint16_t* w_qkvg;       // packed [Wq; Wk; Wv; Wg] ([14336, H], one expert)
+  const uint16_t* w_o;          // packed Wo ([H, 6144])
+  uint16_t* y;                  // [T, H] bf16 out
+  // workspace
+  float* qkvg;                  // [T, 14336] fp32
+  uint16_t* qn;                 // [48][Tp][128], Tp = T rounded up to 128
+  uint16_t* kn;                 // [8][Tp][128]
+  uint16_t* vb;                 // [T][1024]
+  uint16_t* vt;                 // [8][128][Tp]
+  uint16_t* o;                  // [T][6144]
+  int32_t* counts;              // [1]
+  int32_t* offsets;             // [2]
+  int32_t* tile_ctr;            // [32]
+};
+hipError_t launch_attn_proj(hipStream_t s, const AttnArgs& a, int num_cu);
+hipError_t launch_attn_core(hipStream_t s, const AttnArgs& a);
+hipError_t launch_attn_out(hipStream_t s, const AttnArgs& a, int num_cu);
+
+// Plain GEMM on the tiled kernel (one "expert" with every row): out[T, N] =
+// act[T, K] (row-major bf16) x W^T, W packed; FP32 or bf16 out.
+hipError_t launch_plain_tiled(hipStream_t s, const GroupedArgs& a, int num_cu);
 
 // ---- combine / norms (combine.hip) ----
 hipError_t launch_combine(hipStream_t s, const float* o, const int32_t* row_of, const float* w,

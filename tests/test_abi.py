@@ -21,13 +21,14 @@ BIG = 1 << 40
 def declared_functions():
     src = open(HEADER).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(beam_moe_\w+)\s*\(", src)))
+    return sorted(set(re.findall(r"\b(beam_(?:moe|attn)_\w+)\s*\(", src)))
 
 
 def test_header_declares_expected_entry_points():
     names = declared_functions()
     for n in ("beam_moe_route", "beam_moe_permute", "beam_moe_forward", "beam_moe_block",
-              "beam_moe_workspace_bytes", "beam_moe_status_string", "beam_moe_sublayer"):
+              "beam_moe_workspace_bytes", "beam_moe_status_string", "beam_moe_sublayer",
+              "beam_attn_forward", "beam_attn_workspace_bytes"):
         assert n in names
 
 
@@ -150,13 +151,15 @@ def test_permute_and_helpers_validation():
 
 
 def test_timer_api_without_device():
-    assert lib.beam_moe_stage_count() == 6
+    assert lib.beam_moe_stage_count() == 9
     assert lib.beam_moe_stage_name(0) == b"router_logits"
+    assert [lib.beam_moe_stage_name(i) for i in (6, 7, 8)] == [b"attn_proj", b"attn_core",
+                                                               b"attn_out"]
     assert lib.beam_moe_stage_name(99) == b""
     assert lib.beam_moe_timer_begin(0) == -1
     n = ctypes.c_int(0)
-    arr = (ctypes.c_double * 6)()
-    assert lib.beam_moe_timer_end(arr, 6, ctypes.byref(n)) == -1   # not started
+    arr = (ctypes.c_double * 9)()
+    assert lib.beam_moe_timer_end(arr, 9, ctypes.byref(n)) == -1   # not started
 
 
 def test_product_path_does_not_import_oracle():
@@ -171,3 +174,27 @@ def test_product_path_does_not_import_oracle():
         if f.endswith(".py"):
             src = open(os.path.join(ROOT, "oracle", f), encoding="utf-8").read()
             assert "sparse_moe_transformer_group_amd" not in src, f
+
+
+def test_attention_rejects_bad_arguments_on_host():
+    assert lib.beam_attn_workspace_bytes(8192, 5120) >= 8192 * 14336 * 4   # FP32 projections
+    assert lib.beam_attn_workspace_bytes(8192, 100) == 0
+    assert lib.beam_attn_workspace_bytes(-1, 5120) == 0
+    assert lib.beam_attn_workspace_bytes((1 << 16) + 1, 5120) == 0
+    assert lib.beam_attn_workspace_bytes(1 << 15, 32768) == 0         # T * H >= 2^30
+    assert lib.beam_attn_workspace_bytes((1 << 15) - 1, 32768) > 0
+    ws = lib.beam_attn_workspace_bytes(64, 256)
+    f = lib.beam_attn_forward
+
+    def call(T=64, H=256, g=0, win=512, theta=1e4, u=P, wqkvg=P, wo=P, y=P, w=P, nb=ws):
+        return f(None, T, H, g, win, theta, u, wqkvg, wo, y, w, nb)
+    assert call(H=100) == -1
+    assert call(T=-1) == -1
+    assert call(g=2) == -1
+    assert call(win=0) == -1
+    assert call(theta=0.0) == -1
+    assert call(theta=float("nan")) == -1
+    assert call(T=0) == 0                                   # empty sequence: nothing to do
+    assert call(u=None) != 0
+    assert call(nb=ws - 1) == -4
+    assert call(g=1, win=0, theta=0.0, nb=ws - 1) == -4     # window/theta unused on global layers
