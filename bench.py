@@ -49,7 +49,10 @@ def parse():
                    help="untimed warm-up steps (default: at least 5 and at least 0.3 s of work, "
                         "so the timed steps run at settled clocks)")
     p.add_argument("--workload", default="decode",
-                   choices=["decode", "verify", "prefill", "skewed", "stack", "tiny"])
+                   choices=["decode", "verify", "prefill", "skewed", "stack", "tiny",
+                            "attn_swa", "attn_global"],
+                   help="MoE block shapes, or the attention sublayer of a sliding-window "
+                        "(attn_swa) or global (attn_global) layer over one 8192-token sequence")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-sample-tokens", type=int, default=None)
     p.add_argument("--weights", default="bf16", choices=["bf16", "fp8"],
@@ -63,14 +66,15 @@ def parse():
 
 
 def kernel_hash(schedule):
-    with open(GEMM_SRC[schedule], "rb") as f:
+    src = GEMM_SRC.get(schedule, schedule)
+    with open(src, "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def measured_traffic(workload, schedule):
-    """HBM bytes per launch of the gate/up kernel from the committed counter
-    summary, if it was taken on this kernel source."""
-    path = os.path.join(ROOT, "profiles", f"traffic_gateup_{workload}.json")
+def measured_traffic(workload, schedule, kernel="gateup"):
+    """HBM bytes per launch of the kernel from the committed counter summary,
+    if it was taken on this kernel source."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
@@ -80,10 +84,10 @@ def measured_traffic(workload, schedule):
     return d.get("bytes_per_launch")
 
 
-def measured_clock(workload, schedule):
-    """Shader clock and MFMA-busy share of the gate/up kernel from the committed
+def measured_clock(workload, schedule, kernel="gateup"):
+    """Shader clock and MFMA-busy share of the kernel from the committed
     counter summary (GRBM_GUI_ACTIVE, MfmaUtil), if taken on this kernel source."""
-    path = os.path.join(ROOT, "profiles", f"clock_gateup_{workload}.json")
+    path = os.path.join(ROOT, "profiles", f"clock_{kernel}_{workload}.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
@@ -100,6 +104,9 @@ def main():
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(the expert-parallel multi-GPU path is not built)", file=sys.stderr)
         sys.exit(2)
+
+    if args.workload.startswith("attn_"):
+        return run_attention(args)
 
     import numpy as np
     import torch
@@ -291,6 +298,142 @@ def main():
               file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(args, shape, x, wr[0], wg0, wu0, wd0, off)
     print(json.dumps(out), flush=True)
+
+
+ATTN_T, ATTN_H, ATTN_WINDOW = 8192, 5120, 512
+ATTN_Q, ATTN_KV, ATTN_D = 48, 8, 128
+
+
+def attention_pairs(T, window):
+    """Allowed (query, key) pairs: causal, and within the window if one is given."""
+    if window is None:
+        return T * (T + 1) // 2
+    w = min(window, T)
+    return w * (w + 1) // 2 + (T - w) * w
+
+
+def run_attention(args):
+    """Attention sublayer of one sequence (projections, per-head norms and
+    position, flash attention with the sigmoid gate, output projection)."""
+    import torch
+
+    import moe_inputs as MI
+    import sparse_moe_transformer_group_amd as bm
+
+    dev = torch.device("cuda:0")
+    glob = args.workload == "attn_global"
+    T, H = ATTN_T, ATTN_H
+    steps = args.steps if args.steps is not None else 20
+    u = MI.make_attention_input(T, H).to(dev)
+    ws_cpu = MI.make_attention_weights(H)
+    w_qkvg, w_o = bm.pack_attention_weights(*[w.to(dev) for w in ws_cpu])
+    y = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    torch.cuda.synchronize()
+
+    def step():
+        bm.attention(u, w_qkvg, w_o, glob, window=ATTN_WINDOW, out=y)
+
+    if args.warmup is None:
+        torch.cuda.synchronize()
+        t_w, n_w = time.perf_counter(), 0
+        while n_w < 5 or time.perf_counter() - t_w < 0.3:
+            step()
+            n_w += 1
+            if n_w % 5 == 0:
+                torch.cuda.synchronize()
+        args.warmup = n_w
+    else:
+        for _ in range(args.warmup):
+            step()
+    torch.cuda.synchronize()
+
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    with bm.StageTimer(steps) as timer:
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        marks[0].record()
+        for i in range(steps):
+            step()
+            marks[i + 1].record()
+        torch.cuda.synchronize()
+        elapsed = time.perf_counter() - t0
+    step_ms = sorted(marks[i].elapsed_time(marks[i + 1]) for i in range(steps))
+    ms_step = elapsed * 1e3 / steps
+    stage_ms = {n: v / max(timer.calls, 1) for n, v in timer.result.items() if n.startswith("attn_")}
+
+    pairs = attention_pairs(T, None if glob else ATTN_WINDOW)
+    proj_rows = (2 * ATTN_Q + 2 * ATTN_KV) * ATTN_D
+    flops = {"attn_proj": 2 * T * H * proj_rows,
+             "attn_flash": 4 * ATTN_D * pairs * ATTN_Q,
+             "attn_out": 2 * T * ATTN_Q * ATTN_D * H}
+    # algorithmic bytes: each operand read once, each result written once
+    nbytes = {"attn_proj": 2 * T * H + 2 * proj_rows * H + 4 * T * proj_rows,
+              "attn_flash": 2 * T * (ATTN_Q + 2 * ATTN_KV) * ATTN_D + 4 * T * ATTN_Q * ATTN_D
+              + 2 * T * ATTN_Q * ATTN_D,
+              "attn_out": 2 * T * ATTN_Q * ATTN_D + 2 * ATTN_Q * ATTN_D * H + 2 * T * H}
+    total_flops = sum(flops.values())
+    dom = max(flops, key=lambda n: stage_ms[n])
+    kern = {"attn_proj": ("grouped_tiled_kernel<0,...> (q, k, v, gate projection)", "tiled"),
+            "attn_flash": ("attn_flash_kernel", os.path.join(CSRC, "attention.hip")),
+            "attn_out": ("grouped_tiled_kernel<0,...> (output projection)", "tiled")}[dom]
+    ach = flops[dom] / (stage_ms[dom] * 1e-3) / 1e12
+    roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(ach / PEAK_BF16_TFLOPS, 4),
+            "traffic": measured_traffic(args.workload, kern[1], dom),
+            "clock": measured_clock(args.workload, kern[1], dom),
+            "kernel": kern[0], "stage": dom,
+            "algorithmic_per_launch": {"bytes": int(nbytes[dom]), "flops": int(flops[dom])},
+            "avg_launch_ms": round(stage_ms[dom], 5)}
+    per_stage = {n: {"ms": round(stage_ms[n], 5),
+                     "tflops": round(flops[n] / (stage_ms[n] * 1e-3) / 1e12, 1) if n in flops else None}
+                 for n in stage_ms}
+    out = {
+        "metric": "attention-sublayer tokens/s (one sequence, prefill) at H=5120, 48/8 heads x 128",
+        "value": round(T * steps / elapsed, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "ms_per_step_median": round(step_ms[len(step_ms) // 2], 4),
+        "ms_per_step_min": round(step_ms[0], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"beam_{args.workload}", "T": T, "H": H, "q_heads": ATTN_Q,
+                   "kv_heads": ATTN_KV, "head_dim": ATTN_D,
+                   "window": None if glob else ATTN_WINDOW, "attended_pairs": pairs},
+        "tflops": round(total_flops / (ms_step * 1e-3) / 1e12, 1),
+        "frac_peak_mfma": round(total_flops / (ms_step * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+        "stages": per_stage,
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        print(f"[bench] timed loop done ({ms_step:.3f} ms/step); CPU oracle baseline next",
+              file=sys.stderr, flush=True)
+        out["cpu_baseline"] = attention_cpu_baseline(args, u, ws_cpu, glob)
+    print(json.dumps(out), flush=True)
+
+
+def attention_cpu_baseline(args, u, ws_cpu, glob):
+    from threadpoolctl import threadpool_info
+
+    import oracle as O
+    from moe_inputs import bf16_bits
+
+    n = min(args.cpu_sample_tokens or 2048, ATTN_T)
+    ub = bf16_bits(u[:n])
+    wb = [bf16_bits(w) for w in ws_cpu]
+    t0 = time.perf_counter()
+    O.attention_sublayer(ub, *wb, glob, window=ATTN_WINDOW)
+    dt = time.perf_counter() - t0
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    return {"value": round(n / dt, 3), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"a whole {n}-token sequence (the first {n} tokens of the input) through "
+                      f"the FP64 oracle's attention sublayer, {dt:.1f} s; its attention part "
+                      f"per token is {'smaller than at 8192 tokens' if glob else 'the same as at 8192 tokens past the first 512'}"}
 
 
 def cpu_baseline(args, shape, x, wr, wg, wu, wd, off):

@@ -110,7 +110,7 @@ Layout layout(int64_t T, int H, int I, int E, int k) {
 
 // Attention sublayer workspace (Tp = T rounded up to 128).
 struct AttnLayout {
-  size_t qkvg, qn, kn, vb, vt, o, counts, offsets, ctr, total;
+  size_t qkvg, qn, kn, vb, vt, o, vmx, counts, offsets, ctr, total;
 };
 AttnLayout attn_layout(int64_t T) {
   AttnLayout L{};
@@ -127,6 +127,7 @@ AttnLayout attn_layout(int64_t T) {
   L.vb = take((size_t)T * kAttnKVHeads * kAttnHeadDim * 2);
   L.vt = take((size_t)kAttnKVHeads * kAttnHeadDim * Tp * 2);
   L.o = take((size_t)T * kAttnQHeads * kAttnHeadDim * 2);
+  L.vmx = take((size_t)T * kAttnKVHeads * 4);
   L.counts = take(4);
   L.offsets = take(8);
   L.ctr = take(32 * 4);
@@ -187,9 +188,9 @@ bool use_stream(int64_t T, int H, int I, int k, int E) {
 
 // ---------------------------------------------------------------- stage timer
 enum Stage { ST_LOGITS, ST_SELECT, ST_PERMUTE, ST_GATEUP, ST_DOWN, ST_COMBINE,
-             ST_ATT_PROJ, ST_ATT_CORE, ST_ATT_OUT, NST };
+             ST_ATT_PROJ, ST_ATT_PREP, ST_ATT_FLASH, ST_ATT_OUT, NST };
 const char* kStageNames[NST] = {"router_logits", "select", "permute", "gateup", "down", "combine",
-                                "attn_proj", "attn_core", "attn_out"};
+                                "attn_proj", "attn_prep", "attn_flash", "attn_out"};
 
 struct Timer {
   std::mutex mu;
@@ -613,6 +614,7 @@ int beam_attn_forward(void* stream, int64_t T, int H, int global_layer, int wind
              reinterpret_cast<float*>(ws + L.qkvg), reinterpret_cast<uint16_t*>(ws + L.qn),
              reinterpret_cast<uint16_t*>(ws + L.kn), reinterpret_cast<uint16_t*>(ws + L.vb),
              reinterpret_cast<uint16_t*>(ws + L.vt), reinterpret_cast<uint16_t*>(ws + L.o),
+             reinterpret_cast<float*>(ws + L.vmx),
              reinterpret_cast<int32_t*>(ws + L.counts), reinterpret_cast<int32_t*>(ws + L.offsets),
              reinterpret_cast<int32_t*>(ws + L.ctr)};
   hipStream_t st = (hipStream_t)stream;
@@ -621,8 +623,12 @@ int beam_attn_forward(void* stream, int64_t T, int H, int global_layer, int wind
     BEAM_TRY(launch_attn_proj(st, a, num_cu));
   }
   {
-    StageScope sc(slot, ST_ATT_CORE, st);
-    BEAM_TRY(launch_attn_core(st, a));
+    StageScope sc(slot, ST_ATT_PREP, st);
+    BEAM_TRY(launch_attn_prep(st, a));
+  }
+  {
+    StageScope sc(slot, ST_ATT_FLASH, st);
+    BEAM_TRY(launch_attn_flash(st, a));
   }
   {
     StageScope sc(slot, ST_ATT_OUT, st);

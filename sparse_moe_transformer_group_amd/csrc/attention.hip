@@ -49,7 +49,7 @@ __device__ __forceinline__ uint32_t pack_f16x2_rne(float a, float b) {
 // kv head so that the largest |v| lands in [2^14, 2^15), every normal value
 // converts to FP16 exactly and none overflows.  vmax holds the per-head
 // maximum |v| as float bits (non-negative floats order like their bits).
-constexpr int kAttnVmaxSlot = 8;  // tile_ctr[8 .. 15]: the 8 kv heads' max |v|
+constexpr int kAttnVmaxSlot = 8;  // tile_ctr[8 .. 15]: the 8 kv heads' max |v| (float bits)
 __device__ __forceinline__ float attn_v_scale(const int32_t* vmax, int g) {
   const float m = __int_as_float(vmax[g]);
   if (!(m > 0.f) || !isfinite(m)) return 1.f;
@@ -73,28 +73,43 @@ __global__ void attn_setup_kernel(int T, int32_t* counts, int32_t* offsets, int3
 
 // ---------------------------------------------------------------------------
 // prep: one workgroup per token (rows T .. Tp-1 are written as zeros).  Wave
-// w normalises heads w, w+4, ... (48 query heads, then 8 key heads); lane l
-// holds dims l and l+64, which is exactly a RoPE pair.
+// w normalises heads w, w+4, ..., w+52 (48 query heads, then 8 key heads);
+// lane l holds dims l and l+64, which is exactly a RoPE pair.  The largest
+// |v| of each kv head at this token goes to vmx[t][8].
+constexpr int kPrepHeadsPerWave = (kAttnQHeads + kAttnKVHeads) / 4;  // 14
 __global__ __launch_bounds__(256) void attn_prep_kernel(const float* __restrict__ qkvg, int T,
                                                         int global_layer, float theta,
                                                         uint16_t* __restrict__ qn,
                                                         uint16_t* __restrict__ kn,
                                                         uint16_t* __restrict__ vb, int Tp,
-                                                        int32_t* __restrict__ vmax) {
+                                                        float* __restrict__ vmx) {
   const int t = blockIdx.x;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   constexpr int QW = kAttnQHeads * kAttnHeadDim, KW = kAttnKVHeads * kAttnHeadDim;
   constexpr int NW = 2 * QW + 2 * KW;
+  auto dst_of = [&](int h) {
+    return (h < kAttnQHeads) ? qn + ((int64_t)h * Tp + t) * kAttnHeadDim
+                             : kn + ((int64_t)(h - kAttnQHeads) * Tp + t) * kAttnHeadDim;
+  };
   if (t >= T) {  // padding rows of the head-major arrays
-    for (int h = wave; h < kAttnQHeads + kAttnKVHeads; h += 4) {
-      uint16_t* dst = (h < kAttnQHeads) ? qn + ((int64_t)h * Tp + t) * kAttnHeadDim
-                                        : kn + ((int64_t)(h - kAttnQHeads) * Tp + t) * kAttnHeadDim;
+#pragma unroll
+    for (int i = 0; i < kPrepHeadsPerWave; ++i) {
+      uint16_t* dst = dst_of(wave + 4 * i);
       dst[lane] = 0;
       dst[lane + 64] = 0;
     }
     return;
   }
   const float* row = qkvg + (int64_t)t * NW;
+  // all of this wave's loads first (q heads, then k heads: columns h * 128)
+  float x1[kPrepHeadsPerWave], x2[kPrepHeadsPerWave];
+#pragma unroll
+  for (int i = 0; i < kPrepHeadsPerWave; ++i) {
+    const float* src = row + (wave + 4 * i) * kAttnHeadDim;
+    x1[i] = src[lane];
+    x2[i] = src[lane + 64];
+  }
+  const f32x4 v = *reinterpret_cast<const f32x4*>(row + QW + KW + threadIdx.x * 4);
   // rotation of pair `lane` at position t: the angle is formed and reduced in
   // double precision (t * theta^(-lane/64) exceeds FP32 resolution at long
   // positions), then sin/cos in FP32
@@ -106,45 +121,55 @@ __global__ __launch_bounds__(256) void attn_prep_kernel(const float* __restrict_
     const double red = ang - 6.283185307179586 * floor(ang / 6.283185307179586);
     sincosf((float)red, &sn, &cs);
   }
-  for (int h = wave; h < kAttnQHeads + kAttnKVHeads; h += 4) {
-    const bool isq = h < kAttnQHeads;
-    const float* src = isq ? row + h * kAttnHeadDim : row + QW + (h - kAttnQHeads) * kAttnHeadDim;
-    float x1 = src[lane], x2 = src[lane + 64];
-    float ss = x1 * x1 + x2 * x2;
+#pragma unroll
+  for (int i = 0; i < kPrepHeadsPerWave; ++i) {
+    const int h = wave + 4 * i;
+    float a = x1[i], b = x2[i];
+    float ss = a * a + b * b;
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) ss += __shfl_xor(ss, off, 64);
     const float inv = 1.0f / sqrtf(ss * (1.0f / kAttnHeadDim) + 1e-6f);
-    x1 *= inv;
-    x2 *= inv;
+    a *= inv;
+    b *= inv;
     if (global_layer) {
-      if (isq) {
-        x1 *= qs;
-        x2 *= qs;
+      if (h < kAttnQHeads) {
+        a *= qs;
+        b *= qs;
       }
     } else {
-      const float r1 = x1 * cs - x2 * sn, r2 = x2 * cs + x1 * sn;
-      x1 = r1;
-      x2 = r2;
+      const float r1 = a * cs - b * sn, r2 = b * cs + a * sn;
+      a = r1;
+      b = r2;
     }
-    uint16_t* dst = isq ? qn + ((int64_t)h * Tp + t) * kAttnHeadDim
-                        : kn + ((int64_t)(h - kAttnQHeads) * Tp + t) * kAttnHeadDim;
-    const uint32_t p = pack_bf16x2_rne(x1, x2);
+    uint16_t* dst = dst_of(h);
+    const uint32_t p = pack_bf16x2_rne(a, b);
     dst[lane] = (uint16_t)(p & 0xffffu);
     dst[lane + 64] = (uint16_t)(p >> 16);
   }
   // v -> bf16, row-major [T][8*128]; thread i holds dims 4i .. 4i+3, so the
   // 32 lanes of each half-wave hold one kv head
-  {
-    const int c = threadIdx.x * 4;
-    const f32x4 v = *reinterpret_cast<const f32x4*>(row + QW + KW + c);
-    const uint2 b = make_uint2(pack_bf16x2_rne(v[0], v[1]), pack_bf16x2_rne(v[2], v[3]));
-    *reinterpret_cast<uint2*>(vb + (int64_t)t * KW + c) = b;
-    float m = fmaxf(fmaxf(fabsf(__uint_as_float(b.x << 16)), fabsf(__uint_as_float(b.x & 0xffff0000u))),
-                    fmaxf(fabsf(__uint_as_float(b.y << 16)), fabsf(__uint_as_float(b.y & 0xffff0000u))));
+  const uint2 bv = make_uint2(pack_bf16x2_rne(v[0], v[1]), pack_bf16x2_rne(v[2], v[3]));
+  *reinterpret_cast<uint2*>(vb + (int64_t)t * KW + threadIdx.x * 4) = bv;
+  float m = fmaxf(fmaxf(fabsf(__uint_as_float(bv.x << 16)), fabsf(__uint_as_float(bv.x & 0xffff0000u))),
+                  fmaxf(fabsf(__uint_as_float(bv.y << 16)), fabsf(__uint_as_float(bv.y & 0xffff0000u))));
 #pragma unroll
-    for (int off = 16; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
-    if ((threadIdx.x & 31) == 0 && m > 0.f) atomicMax(vmax + (threadIdx.x >> 5), __float_as_int(m));
-  }
+  for (int off = 16; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+  if ((threadIdx.x & 31) == 0) vmx[(int64_t)t * kAttnKVHeads + (threadIdx.x >> 5)] = m;
+}
+
+// vmax[g] = max over tokens of vmx[t][g] (as float bits): one workgroup per kv head
+__global__ __launch_bounds__(256) void attn_vmax_kernel(const float* __restrict__ vmx, int T,
+                                                        int32_t* __restrict__ vmax) {
+  __shared__ float part[4];
+  const int g = blockIdx.x;
+  float m = 0.f;
+  for (int t = threadIdx.x; t < T; t += 256) m = fmaxf(m, vmx[(int64_t)t * kAttnKVHeads + g]);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0)
+    vmax[g] = __float_as_int(fmaxf(fmaxf(part[0], part[1]), fmaxf(part[2], part[3])));
 }
 
 // Key order inside each group of 16 in the transposed v: the attention
@@ -157,8 +182,10 @@ __device__ __forceinline__ int vt_slot(int key) {
   return (key & ~15) | s;
 }
 
-// vt[g][d][slot(t)] = FP16(v[t][g][d] * scale_g) for t < T, zero for
-// T <= t < Tp: 64 x 64 tiles through LDS.  grid (Tp/64, 8 heads x 2 dim halves).
+// v^T tile-major: vt[g][kt][d][64 keys in vt_slot order] = FP16(v[t][g][d] *
+// scale_g) for t = 64 kt + key < T, zero up to Tp, so one 64-key tile of a kv
+// head is one contiguous 16 KB block.  64 x 64 tiles through LDS; grid
+// (Tp/64, 8 heads x 2 dim halves).
 __global__ __launch_bounds__(256) void attn_vt_kernel(const uint16_t* __restrict__ vb, int T,
                                                       int Tp, const int32_t* __restrict__ vmax,
                                                       uint16_t* __restrict__ vt) {
@@ -175,40 +202,67 @@ __global__ __launch_bounds__(256) void attn_vt_kernel(const uint16_t* __restrict
     tile[tt][dd] = __builtin_bit_cast(uint16_t, (_Float16)(v * scale));
   }
   __syncthreads();
+  uint16_t* dst = vt + (((int64_t)g * (Tp / 64) + blockIdx.x) * kAttnHeadDim + d0) * 64;
   for (int i = threadIdx.x; i < 64 * 64; i += 256) {
     const int dd = i >> 6, tt = i & 63;
-    vt[((int64_t)g * kAttnHeadDim + d0 + dd) * Tp + t0 + vt_slot(tt)] = tile[tt][dd];
+    dst[dd * 64 + vt_slot(tt)] = tile[tt][dd];
   }
 }
 
 // ---------------------------------------------------------------------------
-// Flash attention.  grid (Tp/128 query blocks, 48 query heads), 4 waves; wave
-// w owns queries q0 + 32w .. + 31, one per MFMA column (lane l: query l%32).
+// Flash attention.  One workgroup per (query head, 128-query block), 4 waves;
+// wave w owns queries q0 + 32w .. + 31, one per MFMA column (lane l: query l%32).
 //   S^T = K Q^T:  A = 32 keys x 16 dims from LDS, B = the wave's queries from
 //     registers; element i of lane l is key 8(i/4) + 4(l/32) + i%4 of the
 //     32-key tile, query l%32 -- a query's scores sit in one lane and its
-//     partner l^32, so the softmax needs one cross-lane step.
+//     partner l^32, so the softmax needs one cross-lane step (permlane32 swap).
 //   O^T = V^T P^T:  A = 32 dims x 16 keys of the scaled FP16 v^T from LDS
 //     (keys in vt_slot order), B = the lane's own probabilities as FP16.
 //     O^T's columns are queries, so the online-softmax rescale is lane-local.
-// LDS: the 64-key K tile (64 x 256 B) and v^T tile (128 x 128 B), 16-byte
-// chunks XOR-swizzled by row.
-__global__ __launch_bounds__(256) void attn_flash_kernel(const uint16_t* __restrict__ qn,
-                                                         const uint16_t* __restrict__ kn,
-                                                         const uint16_t* __restrict__ vt,
-                                                         const float* __restrict__ qkvg,
-                                                         const int32_t* __restrict__ vmax,
-                                                         int T, int Tp, int window,
-                                                         uint16_t* __restrict__ out) {
-  __shared__ __attribute__((aligned(16))) unsigned char ks[64 * 256];
-  __shared__ __attribute__((aligned(16))) unsigned char vs[128 * 128];
+// Keys go in 64-key tiles, double-buffered in LDS: the next tile's global
+// loads are in flight while the current one is multiplied.  Only tiles that
+// cross the diagonal, the window's edge or the sequence end are masked.
+// The running max is raised lazily: probabilities are formed against a max
+// that may trail the true one by up to 8 (log2 units), so they stay <= 256
+// (exact in FP16 to the same relative precision) and the accumulators are
+// rescaled only when some lane's max grows further; the final o / l is the
+// same softmax.
+// LDS per stage: K tile 64 keys x 256 B, 16-byte chunk c of key j at
+// c ^ (j & 15); v^T tile 128 dims x 128 B, chunk c of dim d at c ^ vt_swz(d).
+// Both are free of bank conflicts for these reads and writes.
+__device__ __forceinline__ int vt_swz(int d) { return (d & 7) ^ (((d >> 2) ^ (d >> 3)) & 1); }
+
+__device__ __forceinline__ float swap_halves_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float swap_halves_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+constexpr int kFlashStage = 32768;  // bytes of one LDS stage (K 16 KB + v^T 16 KB)
+
+__global__ __launch_bounds__(256, 2) void attn_flash_kernel(const uint16_t* __restrict__ qn,
+                                                            const uint16_t* __restrict__ kn,
+                                                            const uint16_t* __restrict__ vt,
+                                                            const float* __restrict__ qkvg,
+                                                            const int32_t* __restrict__ vmax,
+                                                            int T, int Tp, int window,
+                                                            uint16_t* __restrict__ out) {
+  __shared__ __attribute__((aligned(16))) unsigned char lds[2 * kFlashStage];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r = lane & 31, g = lane >> 5;
-  const int h = blockIdx.y, kvh = h / (kAttnQHeads / kAttnKVHeads);
-  const int q0 = blockIdx.x * 128;
-  const int qi = q0 + 32 * wave + r;  // this lane's query
   constexpr int D = kAttnHeadDim;
   constexpr int NW = 2 * kAttnQHeads * D + 2 * kAttnKVHeads * D;
+  constexpr int QPG = kAttnQHeads / kAttnKVHeads;  // query heads per kv head (6)
+  // workgroup b runs on XCD b % 8: XCD x takes every query head of kv head x
+  // (its K and v^T stay in that XCD's L2), longest query blocks first
+  const int nqb = Tp / 128;
+  const int kvh = blockIdx.x & 7, bi = blockIdx.x >> 3;
+  const int h = kvh * QPG + bi % QPG;
+  const int q0 = (nqb - 1 - bi / QPG) * 128;
+  const int qi = q0 + 32 * wave + r;  // this lane's query
 
   // the wave's queries as the B operand: dims 16s + 8g .. + 7 of query qi
   uint4 qf[8];
@@ -223,33 +277,53 @@ __global__ __launch_bounds__(256) void attn_flash_kernel(const uint16_t* __restr
   for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
     for (int i = 0; i < 16; ++i) o[dt][i] = 0.f;
-  float m_run = -INFINITY, l_run = 0.f;
+  float m_run = -INFINITY, l_run = 0.f;  // running max (log2 units), this lane's share of the sum
   const float sc = 1.4426950408889634f / sqrtf((float)D);  // log2(e) / sqrt(D)
 
   const int j_hi = min(q0 + 128, T);  // keys [j_lo, j_hi)
   const int j_lo = window > 0 ? (max(0, q0 - window + 1) & ~63) : 0;
   const uint16_t* kbase = kn + (int64_t)kvh * Tp * D;
-  const uint16_t* vbase = vt + (int64_t)kvh * D * Tp;
+  const uint16_t* vbase = vt + (int64_t)kvh * Tp * D;  // [Tp/64][128][64]
 
-  for (int j0 = j_lo; j0 < j_hi; j0 += 64) {
-    __syncthreads();  // every wave is done with the previous tiles
-    // K tile: thread -> key tid/4, chunks 4(tid%4) .. +3 (16 per 256-B row)
-    {
-      const int key = tid >> 2, c0 = 4 * (tid & 3);
-      const uint4* src = reinterpret_cast<const uint4*>(kbase + (int64_t)(j0 + key) * D);
-#pragma unroll
-      for (int c = 0; c < 4; ++c)
-        *reinterpret_cast<uint4*>(ks + key * 256 + (((c0 + c) ^ (key & 15)) << 4)) = src[c0 + c];
-    }
-    // v^T tile: thread -> dim tid/2, chunks 4(tid%2) .. +3 (8 per 128-B row)
-    {
-      const int d = tid >> 1, c0 = 4 * (tid & 1);
-      const uint4* src = reinterpret_cast<const uint4*>(vbase + (int64_t)d * Tp + j0);
-#pragma unroll
-      for (int c = 0; c < 4; ++c)
-        *reinterpret_cast<uint4*>(vs + d * 128 + (((c0 + c) ^ (d & 7)) << 4)) = src[c0 + c];
-    }
-    __syncthreads();
+  // global -> LDS copy of one tile: 64 contiguous bytes per thread of each
+  // 16 KB tile.  K: key tid/4, chunks 4(tid%4) .. +3.  v^T: dim tid/2,
+  // chunks 4(tid%2) .. +3.
+  const int kkey = tid >> 2, kc0 = 4 * (tid & 3);
+  const int vd = tid >> 1, vh = tid & 1, vsw = vt_swz(vd);
+  // (named registers, not arrays: a private array here would be placed in
+  // scratch or LDS before the loops are unrolled)
+  uint4 k0, k1, k2, k3, v0, v1, v2, v3;
+  auto gload = [&](int j0) {
+    const uint4* ks = reinterpret_cast<const uint4*>(kbase + (int64_t)j0 * D) + tid * 4;
+    const uint4* vs = reinterpret_cast<const uint4*>(vbase + (int64_t)j0 * D) + vd * 8 + 4 * vh;
+    k0 = ks[0]; k1 = ks[1]; k2 = ks[2]; k3 = ks[3];
+    v0 = vs[0]; v1 = vs[1]; v2 = vs[2]; v3 = vs[3];
+  };
+  auto lstore = [&](int stage) {
+    unsigned char* kl = lds + stage * kFlashStage + kkey * 256;
+    unsigned char* vl = lds + stage * kFlashStage + 16384 + vd * 128;
+    const int kx = kkey & 15;
+    *reinterpret_cast<uint4*>(kl + (((kc0 + 0) ^ kx) << 4)) = k0;
+    *reinterpret_cast<uint4*>(kl + (((kc0 + 1) ^ kx) << 4)) = k1;
+    *reinterpret_cast<uint4*>(kl + (((kc0 + 2) ^ kx) << 4)) = k2;
+    *reinterpret_cast<uint4*>(kl + (((kc0 + 3) ^ kx) << 4)) = k3;
+    *reinterpret_cast<uint4*>(vl + (((4 * vh + 0) ^ vsw) << 4)) = v0;
+    *reinterpret_cast<uint4*>(vl + (((4 * vh + 1) ^ vsw) << 4)) = v1;
+    *reinterpret_cast<uint4*>(vl + (((4 * vh + 2) ^ vsw) << 4)) = v2;
+    *reinterpret_cast<uint4*>(vl + (((4 * vh + 3) ^ vsw) << 4)) = v3;
+  };
+
+  if (j_lo < j_hi) {
+    gload(j_lo);
+    lstore(0);
+  }
+  int stage = 0;
+  for (int j0 = j_lo; j0 < j_hi; j0 += 64, stage ^= 1) {
+    __syncthreads();  // tile j0 is in LDS; nobody reads the other stage any more
+    const bool more = j0 + 64 < j_hi;
+    if (more) gload(j0 + 64);
+    const unsigned char* kl = lds + stage * kFlashStage;
+    const unsigned char* vl = kl + 16384;
 
     // S^T for the 64 keys: two 32-key tiles
     f32x16a st[2];
@@ -260,42 +334,50 @@ __global__ __launch_bounds__(256) void attn_flash_kernel(const uint16_t* __restr
       const int key = 32 * t + r;
 #pragma unroll
       for (int s = 0; s < 8; ++s) {
-        const uint4 kf = *reinterpret_cast<const uint4*>(ks + key * 256 + (((2 * s + g) ^ (key & 15)) << 4));
+        const uint4 kf = *reinterpret_cast<const uint4*>(kl + key * 256 + (((2 * s + g) ^ (key & 15)) << 4));
         st[t] = mfma32a(kf, qf[s], st[t]);
       }
     }
-    // mask, scale (log2 domain), running max
+    // mask (edge tiles only) and this tile's max of the raw scores
+    const bool full = j0 + 63 <= q0 && j0 + 63 < T && (window <= 0 || j0 >= q0 + 128 - window);
     float mx = -INFINITY;
+    if (full) {
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, st[t][i]);
+    } else {
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int kj = j0 + 32 * t + 8 * (i >> 2) + 4 * g + (i & 3);
+          const bool ok = kj <= qi && kj < T && (window <= 0 || kj > qi - window);
+          st[t][i] = ok ? st[t][i] : -INFINITY;
+          mx = fmaxf(mx, st[t][i]);
+        }
+    }
+    mx = swap_halves_max(mx) * sc;
+    // lazy rescale, wave-uniform
+    if (__builtin_amdgcn_ballot_w64(mx > m_run + 8.f)) {
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) o[dt][i] *= alpha;
+      l_run *= alpha;
+      m_run = m_new;
+    }
+    const float nm = (m_run == -INFINITY) ? 0.f : -m_run;
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const int kj = j0 + 32 * t + 8 * (i >> 2) + 4 * g + (i & 3);
-        const bool ok = kj <= qi && kj < T && (window <= 0 || kj > qi - window);
-        const float v = ok ? st[t][i] * sc : -INFINITY;
-        st[t][i] = v;
-        mx = fmaxf(mx, v);
-      }
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float m_new = fmaxf(m_run, mx);
-    const float mref = (m_new == -INFINITY) ? 0.f : m_new;
-    const float alpha = exp2f(m_run - mref);
-    float sum = 0.f;
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float p = exp2f(st[t][i] - mref);
+        const float p = __builtin_amdgcn_exp2f(fmaf(st[t][i], sc, nm));
         st[t][i] = p;
-        sum += p;
+        l_run += p;
       }
-    sum += __shfl_xor(sum, 32, 64);
-    l_run = l_run * alpha + sum;
-    m_run = m_new;
-#pragma unroll
-    for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) o[dt][i] *= alpha;
 
     // O^T += V^T P^T: MFMA (t, hf) covers keys 32t + 16hf + 0..15
 #pragma unroll
@@ -310,15 +392,17 @@ __global__ __launch_bounds__(256) void attn_flash_kernel(const uint16_t* __restr
 #pragma unroll
         for (int dt = 0; dt < 4; ++dt) {
           const int d = 32 * dt + r;
-          const uint4 vf = *reinterpret_cast<const uint4*>(vs + d * 128 + ((chunk ^ (d & 7)) << 4));
+          const uint4 vf = *reinterpret_cast<const uint4*>(vl + d * 128 + ((chunk ^ vt_swz(d)) << 4));
           o[dt] = mfma32h(vf, pf, o[dt]);
         }
       }
+    if (more) lstore(stage ^ 1);
   }
 
   // normalise, gate, store: o[dt][i] is dim 32dt + 8(i/4) + 4g + i%4 of query qi
+  const float l_tot = swap_halves_sum(l_run);
   if (qi < T) {
-    const float inv = 1.f / (l_run * attn_v_scale(vmax, kvh));  // both exact up to one rounding
+    const float inv = 1.f / (l_tot * attn_v_scale(vmax, kvh));  // the scale is a power of two
     // gate logits: columns QW + 2 KW .. of the projection output
     const float* gl = qkvg + (int64_t)qi * NW + (kAttnQHeads + 2 * kAttnKVHeads) * D + h * D;
     uint16_t* dst = out + (int64_t)qi * (kAttnQHeads * D) + h * D;
@@ -348,15 +432,23 @@ hipError_t launch_attn_proj(hipStream_t st, const AttnArgs& a, int num_cu) {
   return launch_plain_tiled(st, g, num_cu);
 }
 
-// 2-4. q/k norm and position, v layout, attention with the gate
-hipError_t launch_attn_core(hipStream_t st, const AttnArgs& a) {
+// 2-3. q/k norm and position, v layout
+hipError_t launch_attn_prep(hipStream_t st, const AttnArgs& a) {
   const int Tp = attn_tp(a.T);
-  int32_t* vmax = a.tile_ctr + kAttnVmaxSlot;  // zeroed by attn_setup_kernel
+  int32_t* vmax = a.tile_ctr + kAttnVmaxSlot;
   hipLaunchKernelGGL(attn_prep_kernel, dim3(Tp), dim3(256), 0, st, a.qkvg, (int)a.T, a.global_layer,
-                     a.theta, a.qn, a.kn, a.vb, Tp, vmax);
+                     a.theta, a.qn, a.kn, a.vb, Tp, a.vmx);
+  hipLaunchKernelGGL(attn_vmax_kernel, dim3(kAttnKVHeads), dim3(256), 0, st, a.vmx, (int)a.T, vmax);
   hipLaunchKernelGGL(attn_vt_kernel, dim3(Tp / 64, 2 * kAttnKVHeads), dim3(256), 0, st, a.vb,
                      (int)a.T, Tp, vmax, a.vt);
-  hipLaunchKernelGGL(attn_flash_kernel, dim3(Tp / 128, kAttnQHeads), dim3(256), 0, st, a.qn, a.kn,
+  return hipGetLastError();
+}
+
+// 4. attention with the gate
+hipError_t launch_attn_flash(hipStream_t st, const AttnArgs& a) {
+  const int Tp = attn_tp(a.T);
+  const int32_t* vmax = a.tile_ctr + kAttnVmaxSlot;
+  hipLaunchKernelGGL(attn_flash_kernel, dim3(Tp / 128 * kAttnQHeads), dim3(256), 0, st, a.qn, a.kn,
                      a.vt, a.qkvg, vmax, (int)a.T, Tp, a.global_layer ? 0 : a.window, a.o);
   return hipGetLastError();
 }

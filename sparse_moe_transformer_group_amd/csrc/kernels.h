@@ -101,14 +101,16 @@ struct AttnArgs {
   uint16_t* qn;                 // [48][Tp][128], Tp = T rounded up to 128
   uint16_t* kn;                 // [8][Tp][128]
   uint16_t* vb;                 // [T][1024]
-  uint16_t* vt;                 // [8][128][Tp]
+  uint16_t* vt;                 // [8][128][Tp] FP16, scaled per kv head
   uint16_t* o;                  // [T][6144]
+  float* vmx;                   // [T][8] largest |v| of each kv head per token
   int32_t* counts;              // [1]
   int32_t* offsets;             // [2]
   int32_t* tile_ctr;            // [32]
 };
 hipError_t launch_attn_proj(hipStream_t s, const AttnArgs& a, int num_cu);
-hipError_t launch_attn_core(hipStream_t s, const AttnArgs& a);
+hipError_t launch_attn_prep(hipStream_t s, const AttnArgs& a);   // q/k norm + position, v^T
+hipError_t launch_attn_flash(hipStream_t s, const AttnArgs& a);  // attention + gate -> o
 hipError_t launch_attn_out(hipStream_t s, const AttnArgs& a, int num_cu);
 
 // Plain GEMM on the tiled kernel (one "expert" with every row): out[T, N] =

@@ -151,15 +151,15 @@ def test_permute_and_helpers_validation():
 
 
 def test_timer_api_without_device():
-    assert lib.beam_moe_stage_count() == 9
+    assert lib.beam_moe_stage_count() == 10
     assert lib.beam_moe_stage_name(0) == b"router_logits"
-    assert [lib.beam_moe_stage_name(i) for i in (6, 7, 8)] == [b"attn_proj", b"attn_core",
-                                                               b"attn_out"]
+    assert [lib.beam_moe_stage_name(i) for i in (6, 7, 8, 9)] == [
+        b"attn_proj", b"attn_prep", b"attn_flash", b"attn_out"]
     assert lib.beam_moe_stage_name(99) == b""
     assert lib.beam_moe_timer_begin(0) == -1
     n = ctypes.c_int(0)
-    arr = (ctypes.c_double * 9)()
-    assert lib.beam_moe_timer_end(arr, 9, ctypes.byref(n)) == -1   # not started
+    arr = (ctypes.c_double * 10)()
+    assert lib.beam_moe_timer_end(arr, 10, ctypes.byref(n)) == -1   # not started
 
 
 def test_product_path_does_not_import_oracle():
