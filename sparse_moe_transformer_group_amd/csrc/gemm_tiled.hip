@@ -16,6 +16,8 @@
 // space in XCD-contiguous ranges; weight and token slabs go straight from
 // memory into a 4-stage LDS ring with direct-to-LDS buffer loads.  The
 // decode-size schedule is in gemm_stream.hip.
+#include <algorithm>
+#include <cstdint>
 #include <type_traits>
 
 #include "common.h"
@@ -180,7 +182,7 @@ __global__ __launch_bounds__(256, OCC) void grouped_tiled_kernel(GroupedArgs a) 
   {
     const int e0 = tid * 2;
     int c0 = 0, c1 = 0;
-    if (e0 < E) c0 = NF * ((a.counts[e0] + BM - 1) / BM);
+    if (e0 < E) c0 = NF * (a.m_tiles > 0 ? a.m_tiles : (a.counts[e0] + BM - 1) / BM);
     if (e0 + 1 < E) c1 = NF * ((a.counts[e0 + 1] + BM - 1) / BM);
     s_scan[tid] = c0 + c1;
     __syncthreads();
@@ -249,7 +251,7 @@ __global__ __launch_bounds__(256, OCC) void grouped_tiled_kernel(GroupedArgs a) 
     const int e = __builtin_amdgcn_readfirstlane(elo);
     const int n_e = __builtin_amdgcn_readfirstlane(a.counts[e]);
     const int row0 = __builtin_amdgcn_readfirstlane(a.offsets[e]);
-    const int mt_e = (n_e + BM - 1) / BM;
+    const int mt_e = a.m_tiles > 0 ? a.m_tiles : (n_e + BM - 1) / BM;
     const int rel = tile - __builtin_amdgcn_readfirstlane(s_start[e]);
     // Order of an expert's NF x mt_e tiles.  The 32 CUs of an XCD work on 32
     // consecutive tiles at a time, so consecutive tiles should share data in
@@ -618,8 +620,40 @@ hipError_t launch_down_tiled(hipStream_t st, const GroupedArgs& a, int num_cu) {
   return launch_tiled<1>(st, a, num_cu);
 }
 
+#ifndef BEAM_PLAIN_CFG
+#define BEAM_PLAIN_CFG BEAM_TILED_CFG
+#endif
+template <int BM, int STAGES, int OCC>
+struct PlainBM {
+  static constexpr int value = BM;
+};
+
+// Token tiles of a one-matrix GEMM over T rows: the count mt (tiles of
+// ceil(T / mt) rows or one fewer, at most BM) that minimises the persistent
+// grid's rounds times the tile height, each tile also costing a fixed
+// overhead worth about one 32-row block (prologue, epilogue).
+static int plain_token_tiles(int64_t T, int NF, int nwg, int bm) {
+  const int lo = (int)((T + bm - 1) / bm), hi = (int)std::min<int64_t>((T + 31) / 32, 4 * lo + 64);
+  int best = lo;
+  int64_t best_cost = INT64_MAX;
+  for (int mt = lo; mt <= hi; ++mt) {
+    const int64_t rounds = ((int64_t)NF * mt + nwg - 1) / nwg;
+    const int64_t blocks = ((T + mt - 1) / mt + 31) / 32;
+    const int64_t cost = rounds * (blocks + 1);
+    if (cost < best_cost) {
+      best_cost = cost;
+      best = mt;
+    }
+  }
+  return best;
+}
+
 hipError_t launch_plain_tiled(hipStream_t st, const GroupedArgs& a, int num_cu) {
-  return launch_tiled_cfg<0, false, BEAM_TILED_CFG>(st, a, num_cu);
+  GroupedArgs b = a;
+  constexpr int kPlainBM = PlainBM<BEAM_PLAIN_CFG>::value;
+  const int nwg = ((num_cu + 7) / 8) * 8;
+  if (b.E == 1 && b.Tk > 0) b.m_tiles = plain_token_tiles(b.Tk, (b.N + kBW - 1) / kBW, nwg, kPlainBM);
+  return launch_tiled_cfg<0, false, BEAM_PLAIN_CFG>(st, b, num_cu);
 }
 
 }  // namespace beam

@@ -76,6 +76,8 @@ struct GroupedArgs {
   int* tile_ctr;                // tiled schedule: 8 per-XCD tile-claim counters, zero at
                                 // launch (NULL: static round-robin); unused by the stream path
   int out_bf16;                 // plain tiled GEMM only: 1 = bf16 result, 0 = FP32
+  int m_tiles;                  // tiled schedule, one matrix (E = 1): token tiles to split the
+                                // rows over (0: ceil(rows / tile height)); set by the launcher
 };
 // Decode-size batches: every weight row is streamed once per <= 16*mt tokens.
 hipError_t launch_gateup_stream(hipStream_t s, const GroupedArgs& a, int64_t T, int k);
