@@ -8,3 +8,4 @@ imports the product path.
 from .beam_moe_oracle import *  # noqa: F401,F403
 from .fp8_weights import *  # noqa: F401,F403
 from .beam_attention_oracle import *  # noqa: F401,F403
+from .beam_dense_oracle import *  # noqa: F401,F403
