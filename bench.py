@@ -50,9 +50,10 @@ def parse():
                         "so the timed steps run at settled clocks)")
     p.add_argument("--workload", default="decode",
                    choices=["decode", "verify", "prefill", "skewed", "stack", "tiny",
-                            "attn_swa", "attn_global"],
+                            "attn_swa", "attn_global", "dense_decode", "dense_prefill"],
                    help="MoE block shapes, or the attention sublayer of a sliding-window "
-                        "(attn_swa) or global (attn_global) layer over one 8192-token sequence")
+                        "(attn_swa) or global (attn_global) layer over one 8192-token sequence, "
+                        "or a dense SwiGLU layer (I = 20480) at T = 64 or 8192")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-sample-tokens", type=int, default=None)
     p.add_argument("--weights", default="bf16", choices=["bf16", "fp8"],
@@ -107,6 +108,8 @@ def main():
 
     if args.workload.startswith("attn_"):
         return run_attention(args)
+    if args.workload.startswith("dense_"):
+        return run_dense(args)
 
     import numpy as np
     import torch
@@ -414,6 +417,123 @@ def run_attention(args):
         print(f"[bench] timed loop done ({ms_step:.3f} ms/step); CPU oracle baseline next",
               file=sys.stderr, flush=True)
         out["cpu_baseline"] = attention_cpu_baseline(args, u, ws_cpu, glob)
+    print(json.dumps(out), flush=True)
+
+
+DENSE_H, DENSE_I = 5120, 20480
+# chunks of the intermediate dimension (a pack-time choice): more chunks give
+# a decode-size batch more parallel work; one chunk spares a prefill the FP32
+# chunk partials (measured: 8 chunks 0.155 ms at T = 64, 1 chunk 4.24 ms vs
+# 4.68 ms with 8 at T = 8192)
+DENSE_CHUNKS = {"dense_decode": 8, "dense_prefill": 1}
+
+
+def run_dense(args):
+    """Dense SwiGLU layer (the first three layers), I = 20480, as 8 chunks of
+    its intermediate dimension on the expert GEMMs."""
+    import torch
+
+    import moe_inputs as MI
+    import sparse_moe_transformer_group_amd as bm
+
+    dev = torch.device("cuda:0")
+    T = 64 if args.workload == "dense_decode" else 8192
+    H, I = DENSE_H, DENSE_I
+    steps = args.steps if args.steps is not None else (100 if T == 64 else 20)
+    x = MI.make_x(T, H).to(dev)
+    wg, wu, wd = MI.make_dense_weights(H, I, dev)
+    chunks = DENSE_CHUNKS[args.workload]
+    packed = bm.pack_dense(wg, wu, wd, chunks=chunks)
+    y = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    torch.cuda.synchronize()
+
+    def step():
+        bm.dense_mlp(x, *packed, out=y)
+
+    if args.warmup is None:
+        t_w, n_w = time.perf_counter(), 0
+        while n_w < 5 or time.perf_counter() - t_w < 0.3:
+            step()
+            n_w += 1
+            if n_w % 5 == 0:
+                torch.cuda.synchronize()
+        args.warmup = n_w
+    else:
+        for _ in range(args.warmup):
+            step()
+    torch.cuda.synchronize()
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    with bm.StageTimer(steps) as timer:
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        marks[0].record()
+        for i in range(steps):
+            step()
+            marks[i + 1].record()
+        torch.cuda.synchronize()
+        elapsed = time.perf_counter() - t0
+    step_ms = sorted(marks[i].elapsed_time(marks[i + 1]) for i in range(steps))
+    ms_step = elapsed * 1e3 / steps
+    stage_ms = {n: v / max(timer.calls, 1) for n, v in timer.result.items()
+                if n in ("select", "permute", "gateup", "down", "combine")}
+    flops = 6 * T * H * I
+    wbytes = 3 * H * I * 2
+    gu_ms = stage_ms["gateup"]
+    gu_flops, gu_bytes = 4 * T * H * I, 2 * H * I * 2 + T * H * 2 + T * I * 2
+    schedule = "stream" if T < 20 else "tiled"
+    if gu_flops / gu_bytes < PEAK_BF16_TFLOPS / PEAK_HBM_GBS * 1e3:
+        ach = gu_bytes / (gu_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(ach / PEAK_HBM_GBS, 4)}
+    else:
+        ach = gu_flops / (gu_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4)}
+    roof.update({"traffic": measured_traffic(args.workload, schedule),
+                 "clock": measured_clock(args.workload, schedule),
+                 "kernel": f"grouped_{schedule}_kernel<2,...> (gate/up + SwiGLU)",
+                 "algorithmic_per_launch": {"bytes": int(gu_bytes), "flops": int(gu_flops)},
+                 "avg_launch_ms": round(gu_ms, 5)})
+    out = {
+        "metric": "dense SwiGLU layer tokens/s at H=5120, I=20480",
+        "value": round(T * steps / elapsed, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "ms_per_step_median": round(step_ms[len(step_ms) // 2], 4),
+        "ms_per_step_min": round(step_ms[0], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"beam_{args.workload}", "T": T, "H": H, "I": I, "chunks": chunks},
+        "tflops": round(flops / (ms_step * 1e-3) / 1e12, 1),
+        "frac_peak_mfma": round(flops / (ms_step * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+        "algorithmic_gbs": round((wbytes + 4 * T * H) / (ms_step * 1e-3) / 1e9, 1),
+        "stage_ms": {n: round(v, 5) for n, v in stage_ms.items()},
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        from threadpoolctl import threadpool_info
+
+        import oracle as O
+        from moe_inputs import bf16_bits
+        print(f"[bench] timed loop done ({ms_step:.3f} ms/step); CPU oracle baseline next",
+              file=sys.stderr, flush=True)
+        n = min(args.cpu_sample_tokens or 64, T)
+        hb = [bf16_bits(w) for w in (wg, wu, wd)]     # host copies (not timed)
+        xb = bf16_bits(x[:n])
+        t0 = time.perf_counter()
+        O.dense_mlp(xb, *hb)
+        dt = time.perf_counter() - t0
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+        out["cpu_baseline"] = {"value": round(n / dt, 3), "unit": "tokens/s", "cores": threads,
+                               "kind": "oracle",
+                               "sample": f"first {n} tokens of the batch through the FP64 oracle's dense "
+                                         f"layer (weights staged in host memory beforehand), {dt:.1f} s"}
     print(json.dumps(out), flush=True)
 
 

@@ -259,6 +259,38 @@ int beam_attn_forward(void* stream, int64_t T, int H, int global_layer, int wind
                       void* workspace, size_t workspace_bytes);
 
 /*
+ * Dense SwiGLU layer (the first three layers): page "Willkommen Beam: ein
+ * offenes 501B-Modell, das Sie besitzen, anpassen und skalieren können",
+ * section "Mixture of Experts" (dense layers before the expert layers), with
+ * the expert's SwiGLU and rounding: y = bf16( down( bf16( SiLU(gate x) *
+ * (up x) ) ) ), gate/up and the product in FP32, down accumulated in FP32.
+ * The pages give no intermediate size; I = 20480 (8 x 2560) is the reading
+ * the tests and benchmark use, any I with I / chunks a multiple of 64 works.
+ *
+ *   x        [T, H] bf16
+ *   w_gate   gate [I, H] split into `chunks` row blocks of I / chunks rows,
+ *            i.e. [chunks, I/chunks, H], packed with beam_moe_pack_weights
+ *            (E = chunks, N = I / chunks, K = H); likewise w_up
+ *   w_down   down [H, I] split into column blocks: chunk c is columns
+ *            c*I/chunks .. (c+1)*I/chunks - 1, i.e. [chunks, H, I/chunks],
+ *            packed with E = chunks, N = H, K = I / chunks
+ *   y        [T, H] bf16 out
+ *
+ * The layer runs as the expert path with `chunks` experts, every token sent
+ * to all of them with weight 1: each chunk's down output stays FP32 and the
+ * chunks are summed in order in FP32 before the one bf16 rounding of y (the
+ * same value as one down product over I, up to FP32 summation order).  More
+ * chunks give decode-size batches more parallel work.  Constraints: 1 <=
+ * chunks <= 32, I % chunks == 0, H and I / chunks multiples of 64 in [64,
+ * 32768], 0 <= T <= 2^24.  Workspace: beam_dense_workspace_bytes(T, H, I,
+ * chunks) bytes (0 for invalid sizes).  Errors as for the MoE calls.
+ */
+size_t beam_dense_workspace_bytes(int64_t T, int H, int I, int chunks);
+int beam_dense_mlp(void* stream, int64_t T, int H, int I, int chunks, const uint16_t* x,
+                   const uint16_t* w_gate, const uint16_t* w_up, const uint16_t* w_down, uint16_t* y,
+                   void* workspace, size_t workspace_bytes);
+
+/*
  * Expert-GEMM schedule for later calls in this process: 0 = automatic (the
  * weight-streaming schedule when there are fewer than 20 assignments per
  * expert on average, the LDS-tiled schedule otherwise), 1 = always

@@ -13,6 +13,7 @@ skewed / stacked batches this repository measures.
 
 Value recipe (no trained weights exist here):
   * attention input u ~ N(0, 1) and Wq, Wk, Wv, Wg, Wo ~ N(0, 0.02) -> bf16
+  * dense layer gate, up [I, H] and down [H, I] ~ N(0, 0.02) -> bf16
   * x            ~ N(0, 1)    -> bf16 (round to nearest even)
   * router Wr    ~ N(0, 0.02) -> bf16, layout [E, H]
   * gate, up     ~ N(0, 0.02) -> bf16, layout [E, I, H]
@@ -36,6 +37,7 @@ SEED = 20261016
 # Tensor ids used to derive independent seeds.
 TID_X, TID_WR, TID_WG, TID_WU, TID_WD, TID_ZIPF_PERM, TID_ZIPF_CAL = range(7)
 TID_ATT_U, TID_ATT_WQ, TID_ATT_WK, TID_ATT_WV, TID_ATT_WG, TID_ATT_WO = range(7, 13)
+TID_DENSE_WG, TID_DENSE_WU, TID_DENSE_WD = range(13, 16)
 
 # attention: 48 query heads and 8 key/value heads of 128 dims
 ATT_Q_DIM, ATT_KV_DIM = 48 * 128, 8 * 128
@@ -184,6 +186,20 @@ def make_attention_weights(H: int, layer: int = 0, case: int = 0):
               (TID_ATT_WV, (ATT_KV_DIM, H)), (TID_ATT_WG, (ATT_Q_DIM, H)),
               (TID_ATT_WO, (H, ATT_Q_DIM)))
     return tuple(_cpu_normal(shape, WEIGHT_SIGMA, case, layer, tid, *shape) for tid, shape in shapes)
+
+
+def make_dense_weights(H: int, I: int, device, layer: int = 0, case: int = 0):
+    """Dense SwiGLU layer: gate [I, H], up [I, H], down [H, I] bf16 ~ N(0, 0.02),
+    drawn on `device` (a device generator seeded per tensor)."""
+    device = torch.device(device)
+    out = []
+    for tid, shape in ((TID_DENSE_WG, (I, H)), (TID_DENSE_WU, (I, H)), (TID_DENSE_WD, (H, I))):
+        g = torch.Generator(device=device)
+        g.manual_seed(seed_for(case, layer, tid, H, I))
+        w = torch.randn(shape, generator=g, dtype=torch.float32, device=device)
+        out.append(w.mul_(WEIGHT_SIGMA).to(torch.bfloat16))
+        del w
+    return tuple(out)
 
 
 def bf16_bits(t: torch.Tensor) -> np.ndarray:

@@ -259,9 +259,13 @@ struct Experts {
   const float *sg, *su, *sd;
 };
 
+// exact_rows: every row of the single matrix (E = 1, k = 1) is used, so the
+// tiled GEMMs may pick their token-tile count from T.
 int run_forward(hipStream_t st, int64_t T, int H, int I, int E, int k, const uint16_t* x,
                 const int32_t* ids, const float* w, const Experts& ex, uint16_t* y,
-                int32_t* user_counts, const Layout& L, char* ws, int slot, int num_cu) {
+                int32_t* user_counts, const Layout& L, char* ws, int slot, int num_cu,
+                bool exact_rows = false) {
+  const bool one = exact_rows && E == 1 && k == 1;
   const int64_t Tk = T * k;
   int32_t* counts = reinterpret_cast<int32_t*>(ws + L.counts);
   int32_t* offsets = reinterpret_cast<int32_t*>(ws + L.offsets);
@@ -280,11 +284,13 @@ int run_forward(hipStream_t st, int64_t T, int H, int I, int E, int k, const uin
     StageScope sc(slot, ST_GATEUP, st);
     if (!stream) BEAM_TRY(launch_fill_i32(st, tctr, 16, 0));  // a kernel, not a memset: graph-safe
     GroupedArgs a{x, sorted, ex.wg, ex.wu, ex.sg, ex.su, counts, offsets, h, I, H, E, Tk, tctr};
+    if (one) a.m_tiles = tiled_token_tiles(T, I, 2, num_cu);
     BEAM_TRY(stream ? launch_gateup_stream(st, a, T, k) : launch_gateup_tiled(st, a, num_cu));
   }
   {
     StageScope sc(slot, ST_DOWN, st);
     GroupedArgs a{h, nullptr, ex.wd, nullptr, ex.sd, nullptr, counts, offsets, o, H, I, E, Tk, tctr + 8};
+    if (one) a.m_tiles = tiled_token_tiles(T, H, 1, num_cu);
     BEAM_TRY(stream ? launch_down_stream(st, a, T, k) : launch_down_tiled(st, a, num_cu));
   }
   {
@@ -635,6 +641,50 @@ int beam_attn_forward(void* stream, int64_t T, int H, int global_layer, int wind
     BEAM_TRY(launch_attn_out(st, a, num_cu));
   }
   return BEAM_MOE_OK;
+}
+
+}  // extern "C"
+
+// ---- dense SwiGLU layer as C chunks of its intermediate dimension
+namespace {
+int check_dense_dims(int64_t T, int H, int I, int C) {
+  if (C < 1 || C > kMaxK || I % C != 0) return BEAM_MOE_ERR_INVALID_DIM;
+  return check_forward_dims(T, H, I / C, C, C);
+}
+}  // namespace
+
+extern "C" {
+
+size_t beam_dense_workspace_bytes(int64_t T, int H, int I, int chunks) {
+  if (check_dense_dims(T, H, I, chunks) != BEAM_MOE_OK) return 0;
+  return layout(T, H, I / chunks, chunks, chunks).total;
+}
+
+int beam_dense_mlp(void* stream, int64_t T, int H, int I, int chunks, const uint16_t* x,
+                   const uint16_t* w_gate, const uint16_t* w_up, const uint16_t* w_down, uint16_t* y,
+                   void* workspace, size_t workspace_bytes) {
+  int rc = check_dense_dims(T, H, I, chunks);
+  if (rc) return rc;
+  if (T == 0) return BEAM_MOE_OK;
+  rc = check_ptrs({x, w_gate, w_up, w_down, y, workspace}, {});
+  if (rc) return rc;
+  const int C = chunks, Ic = I / chunks;
+  const Layout L = layout(T, H, Ic, C, C);
+  if (workspace_bytes < L.total) return BEAM_MOE_ERR_WORKSPACE_TOO_SMALL;
+  int num_cu;
+  if ((rc = device_check(&num_cu))) return rc;
+  const int slot = timer_claim();
+  hipStream_t st = (hipStream_t)stream;
+  char* ws = static_cast<char*>(workspace);
+  int32_t* ids = reinterpret_cast<int32_t*>(ws + L.ids);
+  float* w = reinterpret_cast<float*>(ws + L.w);
+  {
+    StageScope sc(slot, ST_SELECT, st);
+    BEAM_TRY(launch_dense_routing(st, ids, w, T, C));
+  }
+  const Experts ex{w_gate, w_up, w_down, nullptr, nullptr, nullptr};
+  return run_forward(st, T, H, Ic, C, C, x, ids, w, ex, y, nullptr, L, ws, slot, num_cu,
+                     /*exact_rows=*/true);
 }
 
 int beam_moe_stage_count(void) { return NST; }

@@ -656,4 +656,10 @@ hipError_t launch_plain_tiled(hipStream_t st, const GroupedArgs& a, int num_cu) 
   return launch_tiled_cfg<0, false, BEAM_PLAIN_CFG>(st, b, num_cu);
 }
 
+int tiled_token_tiles(int64_t rows, int N, int MAT, int num_cu) {
+  const int F = (MAT == 2) ? kBW / 2 : kBW;
+  const int nwg = ((num_cu + 7) / 8) * 8;
+  return plain_token_tiles(rows, (N + F - 1) / F, nwg, 320);
+}
+
 }  // namespace beam

@@ -17,6 +17,8 @@ hipError_t launch_select(hipStream_t s, const float* zpart, int S, const float* 
                          int groups, int topk_groups, int k, float scale, int32_t* ids, float* w,
                          int32_t* counts);
 hipError_t launch_fill_i32(hipStream_t s, int32_t* p, int64_t n, int32_t v);
+// ids[t*C + j] = j, w = 1 (a dense layer as C chunks of its intermediate dimension)
+hipError_t launch_dense_routing(hipStream_t s, int32_t* ids, float* w, int64_t T, int C);
 
 // ---- permutation (permute.hip) ----
 constexpr int kPermChunk = 512;  // assignments per permutation block
@@ -85,6 +87,8 @@ hipError_t launch_down_stream(hipStream_t s, const GroupedArgs& a, int64_t T, in
 // Prefill-size batches: LDS-staged tiles on MFMA, persistent XCD-aware schedule.
 hipError_t launch_gateup_tiled(hipStream_t s, const GroupedArgs& a, int num_cu);
 hipError_t launch_down_tiled(hipStream_t s, const GroupedArgs& a, int num_cu);
+// Token-tile count for one matrix (E = 1) over exactly `rows` rows (GroupedArgs::m_tiles).
+int tiled_token_tiles(int64_t rows, int N, int MAT, int num_cu);
 // ---- attention sublayer (attention.hip) ----
 constexpr int kAttnQHeads = 48, kAttnKVHeads = 8, kAttnHeadDim = 128;
 constexpr int kAttnProjRows = 2 * kAttnQHeads * kAttnHeadDim + 2 * kAttnKVHeads * kAttnHeadDim;  // q,k,v,gate

@@ -215,4 +215,22 @@ hipError_t launch_permute(hipStream_t st, const int32_t* ids, int64_t Tk, int k,
   return hipGetLastError();
 }
 
+// Routing of a dense layer split into C chunks of its intermediate dimension:
+// every token goes to chunk j in slot j with weight 1.
+__global__ __launch_bounds__(256) void dense_routing_kernel(int32_t* __restrict__ ids,
+                                                            float* __restrict__ w, int64_t n, int C) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < n) {
+    ids[i] = (int32_t)(i % C);
+    w[i] = 1.0f;
+  }
+}
+
+hipError_t launch_dense_routing(hipStream_t st, int32_t* ids, float* w, int64_t T, int C) {
+  const int64_t n = T * C;
+  hipLaunchKernelGGL(dense_routing_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, ids, w,
+                     n, C);
+  return hipGetLastError();
+}
+
 }  // namespace beam

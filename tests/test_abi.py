@@ -21,14 +21,15 @@ BIG = 1 << 40
 def declared_functions():
     src = open(HEADER).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(beam_(?:moe|attn)_\w+)\s*\(", src)))
+    return sorted(set(re.findall(r"\b(beam_(?:moe|attn|dense)_\w+)\s*\(", src)))
 
 
 def test_header_declares_expected_entry_points():
     names = declared_functions()
     for n in ("beam_moe_route", "beam_moe_permute", "beam_moe_forward", "beam_moe_block",
               "beam_moe_workspace_bytes", "beam_moe_status_string", "beam_moe_sublayer",
-              "beam_attn_forward", "beam_attn_workspace_bytes"):
+              "beam_attn_forward", "beam_attn_workspace_bytes", "beam_dense_mlp",
+              "beam_dense_workspace_bytes"):
         assert n in names
 
 
@@ -198,3 +199,24 @@ def test_attention_rejects_bad_arguments_on_host():
     assert call(u=None) != 0
     assert call(nb=ws - 1) == -4
     assert call(g=1, win=0, theta=0.0, nb=ws - 1) == -4     # window/theta unused on global layers
+
+
+def test_dense_rejects_bad_arguments_on_host():
+    n = lib.beam_dense_workspace_bytes(8192, 5120, 20480, 8)
+    assert n >= 8192 * 8 * 5120 * 4        # FP32 chunk outputs
+    assert lib.beam_dense_workspace_bytes(64, 5120, 20480, 3) == 0     # I % chunks
+    assert lib.beam_dense_workspace_bytes(64, 5120, 20480, 33) == 0    # chunks > 32
+    assert lib.beam_dense_workspace_bytes(64, 5120, 20480 + 64, 8) == 0  # I / chunks not a multiple of 64
+    assert lib.beam_dense_workspace_bytes(64, 100, 2048, 1) == 0
+    ws = lib.beam_dense_workspace_bytes(64, 256, 512, 2)
+    f = lib.beam_dense_mlp
+
+    def call(T=64, H=256, I=512, C=2, x=P, g=P, u=P, d=P, y=P, w=P, nb=ws):
+        return f(None, T, H, I, C, x, g, u, d, y, w, nb)
+    assert call(C=0) == -1
+    assert call(I=500) == -1
+    assert call(T=-1) == -1
+    assert call(T=0) == 0
+    assert call(g=None) == -2
+    assert call(y=P + 2) == -3
+    assert call(nb=ws - 1) == -4
