@@ -199,7 +199,7 @@ def main():
     step_ms = sorted(marks[i].elapsed_time(marks[i + 1]) for i in range(steps))
     ms_step = elapsed * 1e3 / steps
     launches = timer.calls
-    stage_ms = {n: v / max(launches, 1) for n, v in timer.result.items()}
+    stage_ms = {n: v / max(launches, 1) for n, v in timer.result.items() if not n.startswith("attn_")}
 
     # ---- algorithmic work (per step)
     flops_step = layers * T * (2 * H * E + k * 6 * H * I)
