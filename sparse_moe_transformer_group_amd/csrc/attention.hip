@@ -313,10 +313,18 @@ __global__ __launch_bounds__(256, 2) void attn_flash_kernel(const uint16_t* __re
     *reinterpret_cast<uint4*>(vl + (((4 * vh + 3) ^ vsw) << 4)) = v3;
   };
 
-  if (j_lo < j_hi) {
-    gload(j_lo);
-    lstore(0);
-  }
+  // j_lo <= q0 < j_hi always (q0 < T), so the first tile exists.  The
+  // prologue is unconditional on purpose: a path that skipped it would leave
+  // the query loads pending at the loop head, and the compiler would then
+  // wait for all loads (the next tile's prefetch included) before the first
+  // MFMA of every step.
+  gload(j_lo);
+  lstore(0);
+  // the query registers are complete before the loop (otherwise the loads
+  // sink below the prologue and the loop's MFMAs wait on every load in
+  // flight, the next tile's prefetch included)
+#pragma unroll
+  for (int s = 0; s < 8; ++s) asm volatile("" : "+v"(qf[s].x), "+v"(qf[s].y), "+v"(qf[s].z), "+v"(qf[s].w));
   int stage = 0;
   for (int j0 = j_lo; j0 < j_hi; j0 += 64, stage ^= 1) {
     __syncthreads();  // tile j0 is in LDS; nobody reads the other stage any more
