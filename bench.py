@@ -99,6 +99,18 @@ def measured_clock(workload, schedule, kernel="gateup"):
             "bf16_mfma_peak_at_clock_TFLOPs": d.get("bf16_mfma_peak_at_this_clock_TFLOPs")}
 
 
+def copy_probe(dev):
+    """A plain elementwise copy of known size (reads 1 GiB, writes 1 GiB): the
+    calibration dispatch for the HBM traffic counters."""
+    import torch
+    a = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+    b = torch.empty_like(a)
+    for _ in range(2):
+        torch.neg(a, out=b)
+    torch.cuda.synchronize()
+    del a, b
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -235,13 +247,7 @@ def main():
     roof["avg_launch_ms"] = round(gu_ms, 5)
 
     if args.copy_probe:
-        # plain elementwise copy of known size: reads 1 GiB, writes 1 GiB
-        a = torch.ones(1 << 28, dtype=torch.float32, device=dev)
-        b = torch.empty_like(a)
-        for _ in range(2):
-            torch.neg(a, out=b)
-        torch.cuda.synchronize()
-        del a, b
+        copy_probe(dev)
 
     context = None
     if not args.no_context:
@@ -387,6 +393,8 @@ def run_attention(args):
             "kernel": kern[0], "stage": dom,
             "algorithmic_per_launch": {"bytes": int(nbytes[dom]), "flops": int(flops[dom])},
             "avg_launch_ms": round(stage_ms[dom], 5)}
+    if args.copy_probe:
+        copy_probe(dev)
     per_stage = {n: {"ms": round(stage_ms[n], 5),
                      "tflops": round(flops[n] / (stage_ms[n] * 1e-3) / 1e12, 1) if n in flops else None}
                  for n in stage_ms}
@@ -476,6 +484,8 @@ def run_dense(args):
     ms_step = elapsed * 1e3 / steps
     stage_ms = {n: v / max(timer.calls, 1) for n, v in timer.result.items()
                 if n in ("select", "permute", "gateup", "down", "combine")}
+    if args.copy_probe:
+        copy_probe(dev)
     flops = 6 * T * H * I
     wbytes = 3 * H * I * 2
     gu_ms = stage_ms["gateup"]
