@@ -285,51 +285,46 @@ __global__ __launch_bounds__(256, 2) void attn_flash_kernel(const uint16_t* __re
   const uint16_t* kbase = kn + (int64_t)kvh * Tp * D;
   const uint16_t* vbase = vt + (int64_t)kvh * Tp * D;  // [Tp/64][128][64]
 
-  // global -> LDS copy of one tile: 64 contiguous bytes per thread of each
-  // 16 KB tile.  K: key tid/4, chunks 4(tid%4) .. +3.  v^T: dim tid/2,
-  // chunks 4(tid%2) .. +3.
-  const int kkey = tid >> 2, kc0 = 4 * (tid & 3);
-  const int vd = tid >> 1, vh = tid & 1, vsw = vt_swz(vd);
-  // (named registers, not arrays: a private array here would be placed in
-  // scratch or LDS before the loops are unrolled)
-  uint4 k0, k1, k2, k3, v0, v1, v2, v3;
-  auto gload = [&](int j0) {
-    const uint4* ks = reinterpret_cast<const uint4*>(kbase + (int64_t)j0 * D) + tid * 4;
-    const uint4* vs = reinterpret_cast<const uint4*>(vbase + (int64_t)j0 * D) + vd * 8 + 4 * vh;
-    k0 = ks[0]; k1 = ks[1]; k2 = ks[2]; k3 = ks[3];
-    v0 = vs[0]; v1 = vs[1]; v2 = vs[2]; v3 = vs[3];
-  };
-  auto lstore = [&](int stage) {
-    unsigned char* kl = lds + stage * kFlashStage + kkey * 256;
-    unsigned char* vl = lds + stage * kFlashStage + 16384 + vd * 128;
-    const int kx = kkey & 15;
-    *reinterpret_cast<uint4*>(kl + (((kc0 + 0) ^ kx) << 4)) = k0;
-    *reinterpret_cast<uint4*>(kl + (((kc0 + 1) ^ kx) << 4)) = k1;
-    *reinterpret_cast<uint4*>(kl + (((kc0 + 2) ^ kx) << 4)) = k2;
-    *reinterpret_cast<uint4*>(kl + (((kc0 + 3) ^ kx) << 4)) = k3;
-    *reinterpret_cast<uint4*>(vl + (((4 * vh + 0) ^ vsw) << 4)) = v0;
-    *reinterpret_cast<uint4*>(vl + (((4 * vh + 1) ^ vsw) << 4)) = v1;
-    *reinterpret_cast<uint4*>(vl + (((4 * vh + 2) ^ vsw) << 4)) = v2;
-    *reinterpret_cast<uint4*>(vl + (((4 * vh + 3) ^ vsw) << 4)) = v3;
+  // global -> LDS copy of one tile by direct-to-LDS buffer loads: wave w
+  // fills bytes 4096 w .. 4096 w + 4095 of the K tile and of the v^T tile,
+  // 1 KB per load.  Lane l of a load lands at LDS offset 16 l of its 1 KB,
+  // so each lane fetches the global chunk that belongs in that swizzled
+  // slot: K rows 256 B (4 keys per load, slot l%16 of key l/16), v^T rows
+  // 128 B (8 dims per load, slot l%8 of dim l/8).  Both tiles of 64 keys
+  // start at byte 256 * j0 of their head's array.
+  const __amdgpu_buffer_rsrc_t rs_k = buf_rsrc(kbase, (uint32_t)Tp * D * 2);
+  const __amdgpu_buffer_rsrc_t rs_v = buf_rsrc(vbase, (uint32_t)Tp * D * 2);
+  uint32_t koff[4], voff[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int key = 4 * (4 * wave + i) + (lane >> 4), kc = lane & 15;
+    koff[i] = (uint32_t)(key * 256 + ((kc ^ (key & 15)) << 4));
+    const int d = 8 * (4 * wave + i) + (lane >> 3), vc = lane & 7;
+    voff[i] = (uint32_t)(d * 128 + ((vc ^ vt_swz(d)) << 4));
+  }
+  const uint32_t lds_base = (uint32_t)(uintptr_t)(lds_void*)lds + 4096u * (uint32_t)wave;
+  auto issue = [&](int j0, int stg) {
+    const uint32_t kl = __builtin_amdgcn_readfirstlane(lds_base + (uint32_t)stg * kFlashStage);
+    const uint32_t so = (uint32_t)j0 * (D * 2);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dma16(kl + 1024u * i, koff[i], rs_k, so);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dma16(kl + 16384u + 1024u * i, voff[i], rs_v, so);
   };
 
-  // j_lo <= q0 < j_hi always (q0 < T), so the first tile exists.  The
-  // prologue is unconditional on purpose: a path that skipped it would leave
-  // the query loads pending at the loop head, and the compiler would then
-  // wait for all loads (the next tile's prefetch included) before the first
-  // MFMA of every step.
-  gload(j_lo);
-  lstore(0);
-  // the query registers are complete before the loop (otherwise the loads
-  // sink below the prologue and the loop's MFMAs wait on every load in
-  // flight, the next tile's prefetch included)
+  // j_lo <= q0 < j_hi always (q0 < T), so the first tile exists
+  issue(j_lo, 0);
+  // the query registers are complete before the loop (otherwise their loads
+  // sink into it and its MFMAs wait on every load in flight)
 #pragma unroll
   for (int s = 0; s < 8; ++s) asm volatile("" : "+v"(qf[s].x), "+v"(qf[s].y), "+v"(qf[s].z), "+v"(qf[s].w));
   int stage = 0;
   for (int j0 = j_lo; j0 < j_hi; j0 += 64, stage ^= 1) {
-    __syncthreads();  // tile j0 is in LDS; nobody reads the other stage any more
-    const bool more = j0 + 64 < j_hi;
-    if (more) gload(j0 + 64);
+    // this wave's loads of tile j0 have landed; after the barrier every
+    // wave's have, and nobody reads the other stage any more
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (j0 + 64 < j_hi) issue(j0 + 64, stage ^ 1);
     const unsigned char* kl = lds + stage * kFlashStage;
     const unsigned char* vl = kl + 16384;
 
@@ -404,7 +399,6 @@ __global__ __launch_bounds__(256, 2) void attn_flash_kernel(const uint16_t* __re
           o[dt] = mfma32h(vf, pf, o[dt]);
         }
       }
-    if (more) lstore(stage ^ 1);
   }
 
   // normalise, gate, store: o[dt][i] is dim 32dt + 8(i/4) + 4g + i%4 of query qi

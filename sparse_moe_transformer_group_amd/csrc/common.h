@@ -74,4 +74,25 @@ __device__ __forceinline__ float swiglu(float g, float u) {
 
 __device__ __forceinline__ int wave_lane() { return threadIdx.x & 63; }
 
+// ---- direct-to-LDS buffer loads (tiled GEMM, flash attention)
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Buffer resource over `bytes` bytes at `base` (raw access; word 3 is the
+// gfx9-family raw-buffer format).  Accesses past the end read as 0.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// One direct-to-LDS 16-byte-per-lane buffer load: lane l's 16 bytes at
+// rsrc + voff + soff land at LDS byte lds + 16 l (lds wave-uniform).  Issued
+// from inline asm so the compiler does not track it: its own wait insertion
+// would otherwise order every later LDS read after all of these loads (it
+// cannot tell ring stages apart), draining the pipeline.  Callers order them
+// with an explicit vmcnt wait and a barrier.  No register is written.
+__device__ __forceinline__ void dma16(uint32_t lds, uint32_t voff, __amdgpu_buffer_rsrc_t rs, uint32_t soff) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+               :: "s"(lds), "v"(voff), "s"(rs), "s"(soff)
+               : "memory", "m0");
+}
+
 }  // namespace beam

@@ -82,31 +82,13 @@ constexpr int kBK = 32;                  // k per pipeline step (64 bytes per ro
 static_assert(kBK == kPackK && kBW == 2 * kPackRows, "a k-step is one packed k-block");
 constexpr int kWBytes = kBW * kBK * 2;   // weight slab per step (16 KB)
 
-typedef __attribute__((address_space(3))) void lds_void;
 typedef unsigned int u32x4v __attribute__((ext_vector_type(4)));
-
-// Buffer resource over `bytes` bytes at `base` (raw access; word 3 is the
-// gfx9-family raw-buffer format).  Accesses past the end read as 0.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
-}
 
 // Physical 16-byte chunk of logical chunk c (0..3) in 64-byte row `row`:
 // XOR by ((row >> 1) ^ (row >> 2)) & 3 keeps the 8-lane and the 16-lane
 // groups of ds_read_b128 conflict-free (32 or 64 banks).
 __device__ __forceinline__ int rchunk(int row, int c) { return c ^ pack_swz(row); }
 
-// One direct-to-LDS 16-byte-per-lane buffer load: lane l's 16 bytes at
-// rsrc + voff + soff land at LDS byte lds + 16 l.  Issued from inline asm so
-// the compiler does not track it: its own wait insertion would otherwise
-// order every later LDS read after all of these loads (it cannot tell the
-// ring stages apart), draining the pipeline.  The k-loop orders them itself
-// with an explicit vmcnt wait and a barrier.  No register is written.
-__device__ __forceinline__ void dma16(uint32_t lds, uint32_t voff, __amdgpu_buffer_rsrc_t rs, uint32_t soff) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
-               :: "s"(lds), "v"(voff), "s"(rs), "s"(soff)
-               : "memory", "m0");
-}
 
 // Wait for this wave's direct-to-LDS loads of the current step (at most N
 // younger ones outstanding) and for its LDS reads, then a workgroup barrier
