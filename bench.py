@@ -439,6 +439,7 @@ DENSE_CHUNKS = {"dense_decode": 8, "dense_prefill": 1}
 def run_dense(args):
     """Dense SwiGLU layer (the first three layers), I = 20480, as 8 chunks of
     its intermediate dimension on the expert GEMMs."""
+    import numpy as np
     import torch
 
     import moe_inputs as MI
@@ -451,7 +452,8 @@ def run_dense(args):
     x = MI.make_x(T, H).to(dev)
     wg, wu, wd = MI.make_dense_weights(H, I, dev)
     chunks = DENSE_CHUNKS[args.workload]
-    packed = bm.pack_dense(wg, wu, wd, chunks=chunks)
+    fp8 = args.weights == "fp8"
+    packed = bm.pack_dense(wg, wu, wd, chunks=chunks, fp8=fp8)
     y = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
     torch.cuda.synchronize()
 
@@ -487,9 +489,11 @@ def run_dense(args):
     if args.copy_probe:
         copy_probe(dev)
     flops = 6 * T * H * I
-    wbytes = 3 * H * I * 2
+    wb = 1 if fp8 else 2                                   # bytes per weight
+    sb = (lambda rows: 4 * rows) if fp8 else (lambda rows: 0)  # FP8 row scales
+    wbytes = 3 * H * I * wb + sb(2 * I + chunks * H)
     gu_ms = stage_ms["gateup"]
-    gu_flops, gu_bytes = 4 * T * H * I, 2 * H * I * 2 + T * H * 2 + T * I * 2
+    gu_flops, gu_bytes = 4 * T * H * I, 2 * H * I * wb + sb(2 * I) + T * H * 2 + T * I * 2
     schedule = "stream" if T < 20 else "tiled"
     if gu_flops / gu_bytes < PEAK_BF16_TFLOPS / PEAK_HBM_GBS * 1e3:
         ach = gu_bytes / (gu_ms * 1e-3) / 1e9
@@ -499,8 +503,9 @@ def run_dense(args):
         ach = gu_flops / (gu_ms * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4)}
-    roof.update({"traffic": measured_traffic(args.workload, schedule),
-                 "clock": measured_clock(args.workload, schedule),
+    tag = args.workload + ("_fp8" if fp8 else "")
+    roof.update({"traffic": measured_traffic(tag, schedule),
+                 "clock": measured_clock(tag, schedule),
                  "kernel": f"grouped_{schedule}_kernel<2,...> (gate/up + SwiGLU)",
                  "algorithmic_per_launch": {"bytes": int(gu_bytes), "flops": int(gu_flops)},
                  "avg_launch_ms": round(gu_ms, 5)})
@@ -517,9 +522,10 @@ def run_dense(args):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "fp8-e4m3 weights x bf16 activations" if fp8 else "bf16",
         "data": "synthetic",
-        "config": {"workload": f"beam_{args.workload}", "T": T, "H": H, "I": I, "chunks": chunks},
+        "config": {"workload": f"beam_{args.workload}", "weights": args.weights, "T": T, "H": H,
+                   "I": I, "chunks": chunks},
         "tflops": round(flops / (ms_step * 1e-3) / 1e12, 1),
         "frac_peak_mfma": round(flops / (ms_step * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
         "algorithmic_gbs": round((wbytes + 4 * T * H) / (ms_step * 1e-3) / 1e9, 1),
@@ -535,6 +541,12 @@ def run_dense(args):
               file=sys.stderr, flush=True)
         n = min(args.cpu_sample_tokens or 64, T)
         hb = [bf16_bits(w) for w in (wg, wu, wd)]     # host copies (not timed)
+        if fp8:  # the oracle's own E4M3 encoding, dequantised per chunk (not timed)
+            deq = lambda m: O.dequantize_rows(*O.quantize_rows(m))
+            Ic = I // chunks
+            hb = [deq(hb[0]), deq(hb[1]),
+                  np.concatenate([deq(np.ascontiguousarray(hb[2][:, c * Ic:(c + 1) * Ic]))
+                                  for c in range(chunks)], axis=1)]
         xb = bf16_bits(x[:n])
         t0 = time.perf_counter()
         O.dense_mlp(xb, *hb)

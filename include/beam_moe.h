@@ -289,6 +289,16 @@ size_t beam_dense_workspace_bytes(int64_t T, int H, int I, int chunks);
 int beam_dense_mlp(void* stream, int64_t T, int H, int I, int chunks, const uint16_t* x,
                    const uint16_t* w_gate, const uint16_t* w_up, const uint16_t* w_down, uint16_t* y,
                    void* workspace, size_t workspace_bytes);
+/*
+ * The dense layer with FP8 (E4M3) weights: each chunk matrix packed with
+ * beam_moe_pack_weights_fp8 (E = chunks; one power-of-two scale per row of
+ * each chunk, so the down matrix's scales depend on the chunking), as the
+ * FP8 expert path (beam_moe_forward_fp8).  Same rules and errors.
+ */
+int beam_dense_mlp_fp8(void* stream, int64_t T, int H, int I, int chunks, const uint16_t* x,
+                       const uint8_t* w_gate, const float* s_gate, const uint8_t* w_up,
+                       const float* s_up, const uint8_t* w_down, const float* s_down, uint16_t* y,
+                       void* workspace, size_t workspace_bytes);
 
 /*
  * Expert-GEMM schedule for later calls in this process: 0 = automatic (the

@@ -35,8 +35,12 @@ DENSE_INTERMEDIATE = 8 * 2560
 
 def dense_mlp(x_bits, wg_bits, wu_bits, wd_bits) -> np.ndarray:
     """y = down( bf16( SiLU(gate x) * (up x) ) ) for rows x [T, H] (bf16 bits);
-    gate, up [I, H] and down [H, I] bf16 bits.  Returns y [T, H] float64,
-    unrounded."""
+    gate, up [I, H] and down [H, I] as bf16 bits, or float64 values (weights
+    already dequantised, e.g. from the FP8 encoding).  Returns y [T, H]
+    float64, unrounded."""
     x = bf16_bits_to_f64(np.asarray(x_bits, dtype=np.uint16))
-    wg, wu, wd = (bf16_bits_to_f64(np.asarray(w, dtype=np.uint16)) for w in (wg_bits, wu_bits, wd_bits))
-    return swiglu_expert(x, wg, wu, wd, round_h=True)
+
+    def widen(w):
+        w = np.asarray(w)
+        return w if w.dtype == np.float64 else bf16_bits_to_f64(w.astype(np.uint16))
+    return swiglu_expert(x, widen(wg_bits), widen(wu_bits), widen(wd_bits), round_h=True)

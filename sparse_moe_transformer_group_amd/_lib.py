@@ -72,6 +72,8 @@ def _load():
         "beam_dense_workspace_bytes": (_c_sz, [_c_i64, _c_int, _c_int, _c_int]),
         "beam_dense_mlp": (_c_int, [_c_vp, _c_i64, _c_int, _c_int, _c_int, _c_vp, _c_vp, _c_vp,
                                     _c_vp, _c_vp, _c_vp, _c_sz]),
+        "beam_dense_mlp_fp8": (_c_int, [_c_vp, _c_i64, _c_int, _c_int, _c_int, _c_vp, _c_vp, _c_vp,
+                                        _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_sz]),
         "beam_moe_set_schedule": (_c_int, [_c_int]),
         "beam_moe_stage_count": (_c_int, []),
         "beam_moe_stage_name": (ctypes.c_char_p, [_c_int]),
@@ -462,10 +464,12 @@ def attention(u, w_qkvg, w_o, global_layer, window=512, theta=10000.0, out=None)
 DENSE_CHUNKS = 8
 
 
-def pack_dense(w_gate, w_up, w_down, chunks=DENSE_CHUNKS):
+def pack_dense(w_gate, w_up, w_down, chunks=DENSE_CHUNKS, fp8=False):
     """Packed weights of a dense SwiGLU layer (nn.Linear layouts, bf16):
     gate and up [I, H] as `chunks` row blocks, down [H, I] as `chunks`
-    column blocks (beam_dense_mlp).  Returns (gate, up, down) PackedMatrix."""
+    column blocks (beam_dense_mlp).  Returns (gate, up, down) PackedMatrix,
+    or PackedFP8 (E4M3 codes, a power-of-two scale per row of each chunk)
+    with fp8=True."""
     I, H = w_gate.shape
     if I % chunks:
         raise ValueError(f"I = {I} is not a multiple of chunks = {chunks}")
@@ -474,8 +478,8 @@ def pack_dense(w_gate, w_up, w_down, chunks=DENSE_CHUNKS):
     _dev_tensor(w_down, "w_down", torch.bfloat16, (H, I))
     Ic = I // chunks
     wd = w_down.view(H, chunks, Ic).permute(1, 0, 2).contiguous()     # [chunks, H, Ic]
-    return (pack_weights(w_gate.view(chunks, Ic, H)), pack_weights(w_up.view(chunks, Ic, H)),
-            pack_weights(wd))
+    pack = pack_weights_fp8 if fp8 else pack_weights
+    return pack(w_gate.view(chunks, Ic, H)), pack(w_up.view(chunks, Ic, H)), pack(wd)
 
 
 def dense_workspace_bytes(T: int, H: int, I: int, chunks: int) -> int:
@@ -490,8 +494,9 @@ def dense_mlp(x, w_gate, w_up, w_down, out=None):
     T, H = x.shape
     dev = x.device
     _dev_tensor(x, "x", torch.bfloat16, (T, H))
+    kind = PackedFP8 if isinstance(w_gate, PackedFP8) else PackedMatrix
     for name, m in (("w_gate", w_gate), ("w_up", w_up), ("w_down", w_down)):
-        if not isinstance(m, PackedMatrix):
+        if not isinstance(m, kind):
             raise TypeError(f"{name} must come from pack_dense")
     C, Ic = w_gate.E, w_gate.N
     if (w_gate.K, w_up.E, w_up.N, w_up.K) != (H, C, Ic, H) or (w_down.E, w_down.N, w_down.K) != (C, H, Ic):
@@ -499,6 +504,12 @@ def dense_mlp(x, w_gate, w_up, w_down, out=None):
     y = out if out is not None else torch.empty((T, H), dtype=torch.bfloat16, device=dev)
     _dev_tensor(y, "out", torch.bfloat16, (T, H))
     ws = get_workspace(dev, dense_workspace_bytes(T, H, C * Ic, C))
+    if kind is PackedFP8:
+        rc = lib.beam_dense_mlp_fp8(_stream(dev), T, H, C * Ic, C, _ptr(x), _ptr(w_gate.data),
+                                    _ptr(w_gate.scales), _ptr(w_up.data), _ptr(w_up.scales),
+                                    _ptr(w_down.data), _ptr(w_down.scales), _ptr(y), _ptr(ws), ws.numel())
+        _check("beam_dense_mlp_fp8", rc)
+        return y
     rc = lib.beam_dense_mlp(_stream(dev), T, H, C * Ic, C, _ptr(x), _ptr(w_gate.data), _ptr(w_up.data),
                             _ptr(w_down.data), _ptr(y), _ptr(ws), ws.numel())
     _check("beam_dense_mlp", rc)

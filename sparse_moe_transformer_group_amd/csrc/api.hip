@@ -651,6 +651,27 @@ int check_dense_dims(int64_t T, int H, int I, int C) {
   if (C < 1 || C > kMaxK || I % C != 0) return BEAM_MOE_ERR_INVALID_DIM;
   return check_forward_dims(T, H, I / C, C, C);
 }
+
+// dims and pointers checked by the caller; T > 0
+int dense_common(void* stream, int64_t T, int H, int I, int C, const uint16_t* x, const Experts& ex,
+                 uint16_t* y, void* workspace, size_t workspace_bytes) {
+  const int Ic = I / C;
+  const Layout L = layout(T, H, Ic, C, C);
+  if (workspace_bytes < L.total) return BEAM_MOE_ERR_WORKSPACE_TOO_SMALL;
+  int num_cu, rc;
+  if ((rc = device_check(&num_cu))) return rc;
+  const int slot = timer_claim();
+  hipStream_t st = (hipStream_t)stream;
+  char* ws = static_cast<char*>(workspace);
+  int32_t* ids = reinterpret_cast<int32_t*>(ws + L.ids);
+  float* w = reinterpret_cast<float*>(ws + L.w);
+  {
+    StageScope sc(slot, ST_SELECT, st);
+    BEAM_TRY(launch_dense_routing(st, ids, w, T, C));
+  }
+  return run_forward(st, T, H, Ic, C, C, x, ids, w, ex, y, nullptr, L, ws, slot, num_cu,
+                     /*exact_rows=*/true);
+}
 }  // namespace
 
 extern "C" {
@@ -666,25 +687,22 @@ int beam_dense_mlp(void* stream, int64_t T, int H, int I, int chunks, const uint
   int rc = check_dense_dims(T, H, I, chunks);
   if (rc) return rc;
   if (T == 0) return BEAM_MOE_OK;
-  rc = check_ptrs({x, w_gate, w_up, w_down, y, workspace}, {});
-  if (rc) return rc;
-  const int C = chunks, Ic = I / chunks;
-  const Layout L = layout(T, H, Ic, C, C);
-  if (workspace_bytes < L.total) return BEAM_MOE_ERR_WORKSPACE_TOO_SMALL;
-  int num_cu;
-  if ((rc = device_check(&num_cu))) return rc;
-  const int slot = timer_claim();
-  hipStream_t st = (hipStream_t)stream;
-  char* ws = static_cast<char*>(workspace);
-  int32_t* ids = reinterpret_cast<int32_t*>(ws + L.ids);
-  float* w = reinterpret_cast<float*>(ws + L.w);
-  {
-    StageScope sc(slot, ST_SELECT, st);
-    BEAM_TRY(launch_dense_routing(st, ids, w, T, C));
-  }
+  if ((rc = check_ptrs({x, w_gate, w_up, w_down, y, workspace}, {}))) return rc;
   const Experts ex{w_gate, w_up, w_down, nullptr, nullptr, nullptr};
-  return run_forward(st, T, H, Ic, C, C, x, ids, w, ex, y, nullptr, L, ws, slot, num_cu,
-                     /*exact_rows=*/true);
+  return dense_common(stream, T, H, I, chunks, x, ex, y, workspace, workspace_bytes);
+}
+
+int beam_dense_mlp_fp8(void* stream, int64_t T, int H, int I, int chunks, const uint16_t* x,
+                       const uint8_t* w_gate, const float* s_gate, const uint8_t* w_up,
+                       const float* s_up, const uint8_t* w_down, const float* s_down, uint16_t* y,
+                       void* workspace, size_t workspace_bytes) {
+  int rc = check_dense_dims(T, H, I, chunks);
+  if (rc) return rc;
+  if (T == 0) return BEAM_MOE_OK;
+  if ((rc = check_ptrs({x, w_gate, s_gate, w_up, s_up, w_down, s_down, y, workspace}, {}))) return rc;
+  const Experts ex{reinterpret_cast<const uint16_t*>(w_gate), reinterpret_cast<const uint16_t*>(w_up),
+                   reinterpret_cast<const uint16_t*>(w_down), s_gate, s_up, s_down};
+  return dense_common(stream, T, H, I, chunks, x, ex, y, workspace, workspace_bytes);
 }
 
 int beam_moe_stage_count(void) { return NST; }

@@ -220,3 +220,7 @@ def test_dense_rejects_bad_arguments_on_host():
     assert call(g=None) == -2
     assert call(y=P + 2) == -3
     assert call(nb=ws - 1) == -4
+    f8 = lib.beam_dense_mlp_fp8
+    assert f8(None, 64, 256, 512, 2, P, P, None, P, P, P, P, P, P, ws) == -2      # gate scales missing
+    assert f8(None, 64, 256, 512, 3, P, P, P, P, P, P, P, P, P, ws) == -1         # I % chunks
+    assert f8(None, 0, 256, 512, 2, P, P, P, P, P, P, P, P, P, ws) == 0
