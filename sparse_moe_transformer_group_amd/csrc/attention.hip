@@ -72,11 +72,13 @@ __global__ void attn_setup_kernel(int T, int32_t* counts, int32_t* offsets, int3
 }
 
 // ---------------------------------------------------------------------------
-// prep: one workgroup per token (rows T .. Tp-1 are written as zeros).  Wave
-// w normalises heads w, w+4, ..., w+52 (48 query heads, then 8 key heads);
-// lane l holds dims l and l+64, which is exactly a RoPE pair.  The largest
-// |v| of each kv head at this token goes to vmx[t][8].
-constexpr int kPrepHeadsPerWave = (kAttnQHeads + kAttnKVHeads) / 4;  // 14
+// prep: one workgroup per token (rows T .. Tp-1 are written as zeros).  Each
+// wave normalises pairs of heads: the 28 pairs (q heads 0..47, then k heads)
+// are dealt to the 4 waves, lanes 0..31 taking the first head of a pair and
+// 32..63 the second.  Lane l' = l % 32 holds dims 2l', 2l'+1 and their RoPE
+// partners 2l'+64, 2l'+65, so the rotation needs no cross-lane step.  The
+// largest |v| of each kv head at this token goes to vmx[t][8].
+constexpr int kPrepPairsPerWave = (kAttnQHeads + kAttnKVHeads) / 8;  // 7
 __global__ __launch_bounds__(256) void attn_prep_kernel(const float* __restrict__ qkvg, int T,
                                                         int global_layer, float theta,
                                                         uint16_t* __restrict__ qn,
@@ -85,66 +87,78 @@ __global__ __launch_bounds__(256) void attn_prep_kernel(const float* __restrict_
                                                         float* __restrict__ vmx) {
   const int t = blockIdx.x;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int l = lane & 31, half = lane >> 5;
   constexpr int QW = kAttnQHeads * kAttnHeadDim, KW = kAttnKVHeads * kAttnHeadDim;
   constexpr int NW = 2 * QW + 2 * KW;
   auto dst_of = [&](int h) {
     return (h < kAttnQHeads) ? qn + ((int64_t)h * Tp + t) * kAttnHeadDim
                              : kn + ((int64_t)(h - kAttnQHeads) * Tp + t) * kAttnHeadDim;
   };
+  auto head_of = [&](int i) { return 2 * (wave + 4 * i) + half; };  // q heads 0..47, k heads 48..55
   if (t >= T) {  // padding rows of the head-major arrays
 #pragma unroll
-    for (int i = 0; i < kPrepHeadsPerWave; ++i) {
-      uint16_t* dst = dst_of(wave + 4 * i);
-      dst[lane] = 0;
-      dst[lane + 64] = 0;
+    for (int i = 0; i < kPrepPairsPerWave; ++i) {
+      uint32_t* dst = reinterpret_cast<uint32_t*>(dst_of(head_of(i)));
+      dst[l] = 0u;
+      dst[l + 32] = 0u;
     }
     return;
   }
   const float* row = qkvg + (int64_t)t * NW;
-  // all of this wave's loads first (q heads, then k heads: columns h * 128)
-  float x1[kPrepHeadsPerWave], x2[kPrepHeadsPerWave];
+  // all of this wave's loads first (q and k heads: columns h * 128)
+  float2 lo[kPrepPairsPerWave], hi[kPrepPairsPerWave];
 #pragma unroll
-  for (int i = 0; i < kPrepHeadsPerWave; ++i) {
-    const float* src = row + (wave + 4 * i) * kAttnHeadDim;
-    x1[i] = src[lane];
-    x2[i] = src[lane + 64];
+  for (int i = 0; i < kPrepPairsPerWave; ++i) {
+    const float* src = row + head_of(i) * kAttnHeadDim + 2 * l;
+    lo[i] = *reinterpret_cast<const float2*>(src);
+    hi[i] = *reinterpret_cast<const float2*>(src + 64);
   }
   const f32x4 v = *reinterpret_cast<const f32x4*>(row + QW + KW + threadIdx.x * 4);
-  // rotation of pair `lane` at position t: the angle is formed and reduced in
-  // double precision (t * theta^(-lane/64) exceeds FP32 resolution at long
-  // positions), then sin/cos in FP32
-  float cs = 1.f, sn = 0.f, qs = 1.f;
+  // rotations of pairs 2l' and 2l'+1 at position t: the angle is formed and
+  // reduced in double precision (t * theta^(-i/64) exceeds FP32 resolution at
+  // long positions), then sin/cos in FP32
+  float cs0 = 1.f, sn0 = 0.f, cs1 = 1.f, sn1 = 0.f, qs = 1.f;
   if (global_layer) {
     qs = powf(1.f + (float)(t + 1) / 2048.f, 0.1f);
   } else {
-    const double ang = (double)t * pow((double)theta, -(double)lane / 64.0);
-    const double red = ang - 6.283185307179586 * floor(ang / 6.283185307179586);
-    sincosf((float)red, &sn, &cs);
+    auto angle = [&](int i, float& sn, float& cs) {
+      const double ang = (double)t * pow((double)theta, -(double)i / 64.0);
+      const double red = ang - 6.283185307179586 * floor(ang / 6.283185307179586);
+      sincosf((float)red, &sn, &cs);
+    };
+    angle(2 * l, sn0, cs0);
+    angle(2 * l + 1, sn1, cs1);
   }
 #pragma unroll
-  for (int i = 0; i < kPrepHeadsPerWave; ++i) {
-    const int h = wave + 4 * i;
-    float a = x1[i], b = x2[i];
-    float ss = a * a + b * b;
+  for (int i = 0; i < kPrepPairsPerWave; ++i) {
+    const int h = head_of(i);
+    float a0 = lo[i].x, a1 = lo[i].y, b0 = hi[i].x, b1 = hi[i].y;  // dims 2l', 2l'+1, +64, +65
+    float ss = a0 * a0 + a1 * a1 + b0 * b0 + b1 * b1;
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) ss += __shfl_xor(ss, off, 64);
+    for (int off = 16; off >= 1; off >>= 1) ss += __shfl_xor(ss, off, 64);
     const float inv = 1.0f / sqrtf(ss * (1.0f / kAttnHeadDim) + 1e-6f);
-    a *= inv;
-    b *= inv;
+    a0 *= inv;
+    a1 *= inv;
+    b0 *= inv;
+    b1 *= inv;
     if (global_layer) {
       if (h < kAttnQHeads) {
-        a *= qs;
-        b *= qs;
+        a0 *= qs;
+        a1 *= qs;
+        b0 *= qs;
+        b1 *= qs;
       }
     } else {
-      const float r1 = a * cs - b * sn, r2 = b * cs + a * sn;
-      a = r1;
-      b = r2;
+      const float r0 = a0 * cs0 - b0 * sn0, s0 = b0 * cs0 + a0 * sn0;
+      const float r1 = a1 * cs1 - b1 * sn1, s1 = b1 * cs1 + a1 * sn1;
+      a0 = r0;
+      b0 = s0;
+      a1 = r1;
+      b1 = s1;
     }
-    uint16_t* dst = dst_of(h);
-    const uint32_t p = pack_bf16x2_rne(a, b);
-    dst[lane] = (uint16_t)(p & 0xffffu);
-    dst[lane + 64] = (uint16_t)(p >> 16);
+    uint32_t* dst = reinterpret_cast<uint32_t*>(dst_of(h));
+    dst[l] = pack_bf16x2_rne(a0, a1);       // dims 2l', 2l'+1
+    dst[l + 32] = pack_bf16x2_rne(b0, b1);  // dims 2l'+64, 2l'+65
   }
   // v -> bf16, row-major [T][8*128]; thread i holds dims 4i .. 4i+3, so the
   // 32 lanes of each half-wave hold one kv head
@@ -157,19 +171,26 @@ __global__ __launch_bounds__(256) void attn_prep_kernel(const float* __restrict_
   if ((threadIdx.x & 31) == 0) vmx[(int64_t)t * kAttnKVHeads + (threadIdx.x >> 5)] = m;
 }
 
-// vmax[g] = max over tokens of vmx[t][g] (as float bits): one workgroup per kv head
+// vmax[g] = max over tokens of vmx[t][g] (as float bits, non-negative floats
+// order like their bits): grid (8 kv heads, 16 token slices); each workgroup
+// folds its slice and raises vmax[g] with one atomic (vmax zeroed by
+// attn_setup_kernel).
+constexpr int kVmaxSlices = 16;
 __global__ __launch_bounds__(256) void attn_vmax_kernel(const float* __restrict__ vmx, int T,
                                                         int32_t* __restrict__ vmax) {
   __shared__ float part[4];
   const int g = blockIdx.x;
   float m = 0.f;
-  for (int t = threadIdx.x; t < T; t += 256) m = fmaxf(m, vmx[(int64_t)t * kAttnKVHeads + g]);
+  for (int t = blockIdx.y * 256 + threadIdx.x; t < T; t += 256 * kVmaxSlices)
+    m = fmaxf(m, vmx[(int64_t)t * kAttnKVHeads + g]);
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
   if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = m;
   __syncthreads();
-  if (threadIdx.x == 0)
-    vmax[g] = __float_as_int(fmaxf(fmaxf(part[0], part[1]), fmaxf(part[2], part[3])));
+  if (threadIdx.x == 0) {
+    const float mm = fmaxf(fmaxf(part[0], part[1]), fmaxf(part[2], part[3]));
+    if (mm > 0.f) atomicMax(vmax + g, __float_as_int(mm));
+  }
 }
 
 // Key order inside each group of 16 in the transposed v: the attention
@@ -440,7 +461,7 @@ hipError_t launch_attn_prep(hipStream_t st, const AttnArgs& a) {
   int32_t* vmax = a.tile_ctr + kAttnVmaxSlot;
   hipLaunchKernelGGL(attn_prep_kernel, dim3(Tp), dim3(256), 0, st, a.qkvg, (int)a.T, a.global_layer,
                      a.theta, a.qn, a.kn, a.vb, Tp, a.vmx);
-  hipLaunchKernelGGL(attn_vmax_kernel, dim3(kAttnKVHeads), dim3(256), 0, st, a.vmx, (int)a.T, vmax);
+  hipLaunchKernelGGL(attn_vmax_kernel, dim3(kAttnKVHeads, kVmaxSlices), dim3(256), 0, st, a.vmx, (int)a.T, vmax);
   hipLaunchKernelGGL(attn_vt_kernel, dim3(Tp / 64, 2 * kAttnKVHeads), dim3(256), 0, st, a.vb,
                      (int)a.T, Tp, vmax, a.vt);
   return hipGetLastError();
