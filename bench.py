@@ -61,6 +61,8 @@ def parse():
                         "scales (bf16 activations)")
     p.add_argument("--no-context", action="store_true",
                    help="skip the dense bf16 GEMM context measurement")
+    p.add_argument("--no-graph", action="store_true",
+                   help="skip the HIP-graph replay measurement reported beside the eager value")
     p.add_argument("--copy-probe", action="store_true",
                    help="also run one 1 GiB device copy (HBM counter calibration)")
     return p.parse_args()
@@ -249,6 +251,29 @@ def main():
     if args.copy_probe:
         copy_probe(dev)
 
+    # the same step replayed from a HIP graph (serving-loop style: no launch
+    # overhead between the kernels); reported beside the eager value
+    graph = None
+    if not args.no_graph:
+        step()                    # outputs and workspace exist before the capture
+        torch.cuda.synchronize()
+        gr = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gr):
+            step()
+        for _ in range(3):
+            gr.replay()
+        torch.cuda.synchronize()
+        g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        g0.record()
+        for _ in range(steps):
+            gr.replay()
+        g1.record()
+        torch.cuda.synchronize()
+        gms = g0.elapsed_time(g1) / steps
+        graph = {"ms_per_step": round(gms, 4), "tokens_per_s": round(T / (gms * 1e-3), 1),
+                 "how": f"{steps} replays of one captured step, HIP events around them"}
+        del gr
+
     context = None
     if not args.no_context:
         # what a dense library GEMM sustains on this machine (hipBLASLt through
@@ -298,6 +323,7 @@ def main():
         "frac_peak_hbm": round(gbs / PEAK_HBM_GBS, 4),
         "stage_ms": {n: round(v, 5) for n, v in stage_ms.items()},
         "roofline": roof,
+        "graph_replay": graph,
         "context": context,
     }
 
