@@ -92,6 +92,27 @@ __global__ __launch_bounds__(256) void grouped_stream_kernel(GroupedArgs a) {
     const int rw = grp * 16 + j;                      // row of the wave's LDS tile
     lo[i] = rw * RB8 + (((4 * kbl + c) ^ (rw & 15)) * CH);
   }
+  // FP8: 16-byte loads instead -- load i covers k-block i of all 32 rows
+  // (1 KB): lane l takes row l/2 and physical chunks 2(l%2), 2(l%2)+1 of it,
+  // stored to the LDS slots of their logical chunks (same tile layout).
+  constexpr int LD8 = 4;
+  const unsigned char* lp8[LD8];
+  int lo8[LD8][2];
+  if constexpr (W8) {
+    static_assert(ROWS == 32, "32 rows per wave");
+    const int j = lane >> 1, hh = lane & 1;
+    const int m = j / (RB * 16), rib = rib0 + j % (RB * 16);
+    const unsigned char* base = reinterpret_cast<const unsigned char*>(m == 0 ? a.w0 : a.w1);
+#pragma unroll
+    for (int i = 0; i < LD8; ++i) {
+      lp8[i] = base + e * ebytes + ((int64_t)(rb * nkb + i) * kPackRows + rib) * RBYTES + hh * 16;
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int c = (2 * hh + u) ^ pack8_swz(rib);
+        lo8[i][u] = j * RB8 + (((4 * i + c) ^ (j & 15)) * CH);
+      }
+    }
+  }
 
   for (int c0 = 0; c0 < n_e; c0 += 16 * MT) {
     const uint16_t* bp[MT];
@@ -113,14 +134,15 @@ __global__ __launch_bounds__(256) void grouped_stream_kernel(GroupedArgs a) {
         for (int j = 0; j < MT; ++j) acc[m][i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     const int nsteps = K / 128;  // K is a multiple of 64; a 64-wide tail is handled below
-    uint4 R[W8 ? 1 : LD];
-    uint2 R8[W8 ? LD : 1];
+    uint4 R[W8 ? LD8 : LD];
     uint4 B[2][MT][4];
     auto load_w = [&](int ks) {
+      if constexpr (W8) {
 #pragma unroll
-      for (int i = 0; i < LD; ++i) {
-        if constexpr (W8) R8[i] = ld8_nt(lp[i] + (int64_t)ks * 4 * BLK);
-        else R[i] = ld16_nt(lp[i] + (int64_t)ks * 4 * BLK);
+        for (int i = 0; i < LD8; ++i) R[i] = ld16_nt(lp8[i] + (int64_t)ks * 4 * BLK);
+      } else {
+#pragma unroll
+        for (int i = 0; i < LD; ++i) R[i] = ld16_nt(lp[i] + (int64_t)ks * 4 * BLK);
       }
     };
     auto load_b = [&](int buf, int ks) {
@@ -132,10 +154,15 @@ __global__ __launch_bounds__(256) void grouped_stream_kernel(GroupedArgs a) {
     };
     auto step = [&](int buf, int ks) {
       // slab of step ks: registers -> LDS tile, then prefetch step ks+1
+      if constexpr (W8) {
 #pragma unroll
-      for (int i = 0; i < LD; ++i) {
-        if constexpr (W8) *reinterpret_cast<uint2*>(tile + lo[i]) = R8[i];
-        else st16(tile + lo[i], R[i]);
+        for (int i = 0; i < LD8; ++i) {
+          *reinterpret_cast<uint2*>(tile + lo8[i][0]) = make_uint2(R[i].x, R[i].y);
+          *reinterpret_cast<uint2*>(tile + lo8[i][1]) = make_uint2(R[i].z, R[i].w);
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < LD; ++i) st16(tile + lo[i], R[i]);
       }
       __builtin_amdgcn_wave_barrier();
       if (ks + 1 < nsteps) {
