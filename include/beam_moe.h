@@ -223,6 +223,15 @@ int beam_moe_sublayer(void* stream, int64_t T, int H, int I, int E, int groups, 
                       const uint16_t* w_down, uint16_t* moe_input, uint16_t* moe_output,
                       int32_t* topk_ids, float* topk_weights, int32_t* expert_counts,
                       void* workspace, size_t workspace_bytes);
+/* beam_moe_sublayer with FP8 (E4M3) expert weights and per-row scales, as
+ * beam_moe_block_fp8.  Scale pointers must not be NULL. */
+int beam_moe_sublayer_fp8(void* stream, int64_t T, int H, int I, int E, int groups, int topk_groups,
+                          int k, float scale, float eps, int step, float* stream_io,
+                          const uint16_t* w_router, const uint8_t* w_gate, const float* s_gate,
+                          const uint8_t* w_up, const float* s_up, const uint8_t* w_down,
+                          const float* s_down, uint16_t* moe_input, uint16_t* moe_output,
+                          int32_t* topk_ids, float* topk_weights, int32_t* expert_counts,
+                          void* workspace, size_t workspace_bytes);
 
 /*
  * Attention sublayer of one sequence (prefill): page "Willkommen Beam: ein

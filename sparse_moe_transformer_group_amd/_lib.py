@@ -74,6 +74,10 @@ def _load():
                                     _c_vp, _c_vp, _c_vp, _c_sz]),
         "beam_dense_mlp_fp8": (_c_int, [_c_vp, _c_i64, _c_int, _c_int, _c_int, _c_vp, _c_vp, _c_vp,
                                         _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_sz]),
+        "beam_moe_sublayer_fp8": (_c_int, [_c_vp, _c_i64, _c_int, _c_int, _c_int, _c_int, _c_int,
+                                           _c_int, _c_f, _c_f, _c_int, _c_vp, _c_vp, _c_vp, _c_vp,
+                                           _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp,
+                                           _c_vp, _c_vp, _c_sz]),
         "beam_moe_set_schedule": (_c_int, [_c_int]),
         "beam_moe_stage_count": (_c_int, []),
         "beam_moe_stage_name": (ctypes.c_char_p, [_c_int]),
@@ -392,9 +396,9 @@ def residual_update(stream_io, y, step, eps=1e-6):
 def sublayer(stream_io, step, w_router, w_gate, w_up, w_down, groups=8, topk_groups=4, k=8,
              scale=2.5, eps=1e-6, keep_io=True):
     """One sandwich-normed MoE sublayer + residual update, in place on stream_io
-    (bf16 packed expert weights).  Returns (moe_input, moe_output, ids, weights,
-    counts) when keep_io."""
-    E, I, H = _expert_shapes(w_gate, w_up, w_down, allow_fp8=False)
+    (expert weights from pack_experts or pack_experts_fp8).  Returns
+    (moe_input, moe_output, ids, weights, counts) when keep_io."""
+    E, I, H = _expert_shapes(w_gate, w_up, w_down)
     T = stream_io.shape[0]
     dev = stream_io.device
     _dev_tensor(stream_io, "stream", torch.float32, (T, H))
@@ -407,6 +411,15 @@ def sublayer(stream_io, step, w_router, w_gate, w_up, w_down, groups=8, topk_gro
         w = torch.empty((T, k), dtype=torch.float32, device=dev)
         counts = torch.empty((E,), dtype=torch.int32, device=dev)
     ws = get_workspace(dev, workspace_bytes(T, H, I, E, k))
+    if isinstance(w_gate, PackedFP8):
+        rc = lib.beam_moe_sublayer_fp8(_stream(dev), T, H, I, E, groups, topk_groups, k, float(scale),
+                                       float(eps), int(step), _ptr(stream_io), _ptr(w_router),
+                                       _ptr(w_gate.data), _ptr(w_gate.scales), _ptr(w_up.data),
+                                       _ptr(w_up.scales), _ptr(w_down.data), _ptr(w_down.scales),
+                                       _ptr(xin), _ptr(yb), _ptr(ids), _ptr(w), _ptr(counts), _ptr(ws),
+                                       ws.numel())
+        _check("beam_moe_sublayer_fp8", rc)
+        return (xin, yb, ids, w, counts) if keep_io else None
     rc = lib.beam_moe_sublayer(_stream(dev), T, H, I, E, groups, topk_groups, k, float(scale),
                                float(eps), int(step), _ptr(stream_io), _ptr(w_router), _ptr(w_gate.data),
                                _ptr(w_up.data), _ptr(w_down.data), _ptr(xin), _ptr(yb), _ptr(ids), _ptr(w),

@@ -546,20 +546,23 @@ int beam_moe_residual_update(void* stream, int64_t T, int H, float eps, int step
   return BEAM_MOE_OK;
 }
 
-int beam_moe_sublayer(void* stream, int64_t T, int H, int I, int E, int groups, int topk_groups, int k,
-                      float scale, float eps, int step, float* stream_io, const uint16_t* w_router,
-                      const uint16_t* w_gate, const uint16_t* w_up, const uint16_t* w_down,
-                      uint16_t* moe_input, uint16_t* moe_output, int32_t* topk_ids,
-                      float* topk_weights, int32_t* expert_counts, void* workspace,
-                      size_t workspace_bytes) {
+}  // extern "C"
+
+namespace {
+int sublayer_common(void* stream, int64_t T, int H, int I, int E, int groups, int topk_groups, int k,
+                    float scale, float eps, int step, float* stream_io, const uint16_t* w_router,
+                    const Experts& ex, uint16_t* moe_input, uint16_t* moe_output, int32_t* topk_ids,
+                    float* topk_weights, int32_t* expert_counts, void* workspace,
+                    size_t workspace_bytes) {
   int rc = check_route_dims(T, H, E, groups, topk_groups, k, scale);
   if (rc) return rc;
   if ((rc = check_forward_dims(T, H, I, E, k))) return rc;
   if (step < 2 || !(eps >= 0.f) || !isfinite(eps)) return BEAM_MOE_ERR_INVALID_DIM;
   if (T == 0) return BEAM_MOE_OK;
-  rc = check_ptrs({stream_io, w_router, w_gate, w_up, w_down, workspace},
+  rc = check_ptrs({stream_io, w_router, ex.wg, ex.wu, ex.wd, workspace},
                   {moe_input, moe_output, topk_ids, topk_weights, expert_counts});
   if (rc) return rc;
+  if (ex.sg && (rc = check_ptrs({ex.sg, ex.su, ex.sd}, {}))) return rc;
   const Layout L = layout(T, H, I, E, k);
   if (workspace_bytes < L.total) return BEAM_MOE_ERR_WORKSPACE_TOO_SMALL;
   int num_cu;
@@ -575,12 +578,41 @@ int beam_moe_sublayer(void* stream, int64_t T, int H, int I, int E, int groups, 
   rc = run_route(st, T, H, E, groups, topk_groups, k, scale, xin, w_router, nullptr, ids, w, nullptr,
                  L, ws, slot);
   if (rc) return rc;
-  const Experts ex{w_gate, w_up, w_down, nullptr, nullptr, nullptr};
   rc = run_forward(st, T, H, I, E, k, xin, ids, w, ex, yb, expert_counts, L, ws,
                    slot, num_cu);
   if (rc) return rc;
   BEAM_TRY(launch_residual(st, yb, stream_io, T, H, eps, step));
   return BEAM_MOE_OK;
+}
+}  // namespace
+
+extern "C" {
+
+int beam_moe_sublayer(void* stream, int64_t T, int H, int I, int E, int groups, int topk_groups, int k,
+                      float scale, float eps, int step, float* stream_io, const uint16_t* w_router,
+                      const uint16_t* w_gate, const uint16_t* w_up, const uint16_t* w_down,
+                      uint16_t* moe_input, uint16_t* moe_output, int32_t* topk_ids,
+                      float* topk_weights, int32_t* expert_counts, void* workspace,
+                      size_t workspace_bytes) {
+  const Experts ex{w_gate, w_up, w_down, nullptr, nullptr, nullptr};
+  return sublayer_common(stream, T, H, I, E, groups, topk_groups, k, scale, eps, step, stream_io,
+                         w_router, ex, moe_input, moe_output, topk_ids, topk_weights, expert_counts,
+                         workspace, workspace_bytes);
+}
+
+int beam_moe_sublayer_fp8(void* stream, int64_t T, int H, int I, int E, int groups, int topk_groups,
+                          int k, float scale, float eps, int step, float* stream_io,
+                          const uint16_t* w_router, const uint8_t* w_gate, const float* s_gate,
+                          const uint8_t* w_up, const float* s_up, const uint8_t* w_down,
+                          const float* s_down, uint16_t* moe_input, uint16_t* moe_output,
+                          int32_t* topk_ids, float* topk_weights, int32_t* expert_counts,
+                          void* workspace, size_t workspace_bytes) {
+  if (!s_gate || !s_up || !s_down) return BEAM_MOE_ERR_NULL_POINTER;
+  const Experts ex{reinterpret_cast<const uint16_t*>(w_gate), reinterpret_cast<const uint16_t*>(w_up),
+                   reinterpret_cast<const uint16_t*>(w_down), s_gate, s_up, s_down};
+  return sublayer_common(stream, T, H, I, E, groups, topk_groups, k, scale, eps, step, stream_io,
+                         w_router, ex, moe_input, moe_output, topk_ids, topk_weights, expert_counts,
+                         workspace, workspace_bytes);
 }
 
 // ---------------------------------------------------------------- schedule / timer

@@ -152,3 +152,33 @@ def test_beam_fp8_sampled(bm, beam_fp8, name):
     ref = oracle_fp8_block(bf16_bits(x)[toks], wr, wg, wu, wd, shape, experts=experts)
     st = check_output(y[torch.from_numpy(toks).to(DEV)], ref["y"])
     print(st, flush=True)
+
+
+@pytest.mark.parametrize("schedule", ["stream", "tiled"])
+def test_sublayer_fp8_teacher_forced(bm, schedule):
+    """Two stacked sublayers with FP8 expert weights, each checked with the
+    device's own layer input against the oracle on its dequantised E4M3
+    encoding; the residual update from the device's own output."""
+    shape = BlockShape(T=128, H=256, I=128)
+    print(f"[case] fp8 sublayer schedule={schedule}", flush=True)
+    x = MI.make_x(shape.T, shape.H, case=14).to(DEV)
+    stream = bm.stream_init(x)
+    bm.set_schedule(schedule)
+    try:
+        for step in (2, 3):
+            layer = step - 2
+            wr = MI.make_router(shape.E, shape.H, layer=layer, case=14).to(DEV)
+            wg, wu, wd = MI.make_expert_weights(shape.E, shape.H, shape.I, DEV, layer=layer, case=14)
+            prev = stream.clone()
+            xin, yb, ids, w, counts = bm.sublayer(stream, step, wr, *bm.pack_experts_fp8(wg, wu, wd))
+            sync()
+            prev64 = prev.cpu().numpy().astype(np.float64)
+            blk = O.stack_sublayer(prev64, step, bf16_bits(wr), fp8_experts_oracle(wg, wu, wd),
+                                   shape.groups, shape.topk_groups, shape.k, shape.scale,
+                                   moe_input_bits=bf16_bits(xin))
+            check_routing(ids, w, blk, shape.E, counts)
+            print(check_output(yb, blk["y"], keep_mask(blk)))
+            ref_stream = O.residual_step(prev64, O.rmsnorm(O.bf16_bits_to_f64(bf16_bits(yb))), step)
+            np.testing.assert_allclose(stream.cpu().numpy(), ref_stream, rtol=1e-5, atol=1e-5)
+    finally:
+        bm.set_schedule("auto")
