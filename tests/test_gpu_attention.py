@@ -86,3 +86,12 @@ FULL_ROWS = [0, 1, 63, 127, 128, 511, 512, 513, 1000, 4095, 4096, 6143, 8190, 81
 @pytest.mark.parametrize("global_layer", [False, True])
 def test_attention_full_shape_sampled_rows(bm, global_layer):
     print(run_case(bm, 8192, 5120, global_layer, rows=FULL_ROWS))
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("global_layer", [False, True])
+def test_attention_long_sequence_sampled_rows(bm, global_layer):
+    """Positions up to 20000 (RoPE angles far beyond FP32 resolution of the
+    product pos * theta^(-i/64)); T not a multiple of the 128-query tile."""
+    rows = [0, 511, 512, 10000, 19487, 19488, 19999]
+    print(run_case(bm, 20000, 1024, global_layer, rows=rows, case=7))
