@@ -52,7 +52,15 @@ hipError_t launch_pack(hipStream_t s, const uint16_t* src, uint16_t* dst, int E,
 // smallest power of two with max|W[r,:]| <= 448 * 2^e_r; a code is the E4M3
 // value nearest to W * 2^-e_r (ties to even); the weight is value * 2^e_r.
 constexpr int kPack8BlockBytes = kPackRows * kPackK;
-__host__ __device__ inline int pack8_swz(int row) { return (row >> 3) & 3; }
+// The swizzle depends on row bits 2..4 only (so it is the same for row r of
+// every 32-row block): the four rows that share a bank set under 8-byte
+// operand reads -- rows r, r+4, r+8, r+12 when 16 lanes are served over 32
+// banks, rows r, r+8, r+16, r+24 when 32 lanes are served over 64 -- get
+// four different chunk positions.  A swizzle by bits 3..4 alone leaves the
+// first case 2-way conflicted (measured: SQ_LDS_BANK_CONFLICT).
+__host__ __device__ inline int pack8_swz(int row) {
+  return (((row >> 2) ^ (row >> 4)) & 1) | ((row >> 2) & 2);
+}
 __host__ __device__ inline int64_t packed8_expert_bytes(int N, int K) {
   return (int64_t)((N + kPackRows - 1) / kPackRows) * (K / kPackK) * kPack8BlockBytes;
 }

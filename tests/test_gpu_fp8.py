@@ -27,11 +27,13 @@ def bm():
 def unpack_fp8(data, E, N, K):
     """Codes [E, N, K] from the packed FP8 layout (numpy index arithmetic:
     blocks of 128 rows x 32 k in (row block, k-block) order, 8-byte chunk c of
-    block row j stored at c ^ ((j >> 3) & 3))."""
+    block row j stored at c ^ s(j), s(j) = (j2 ^ j4) + 2 j3 from bits 2..4
+    of j)."""
     NB, KB = -(-N // 128), K // 32
     b = np.asarray(data).reshape(E, NB, KB, 128, 4, 8)
     j = np.arange(128)[:, None]
-    phys = np.arange(4)[None, :] ^ ((j >> 3) & 3)      # logical chunk c sits at phys[j, c]
+    s = (((j >> 2) ^ (j >> 4)) & 1) | ((j >> 2) & 2)
+    phys = np.arange(4)[None, :] ^ s                    # logical chunk c sits at phys[j, c]
     logical = b[:, :, :, j, phys, :]                    # e, rb, kb, j, c, 8
     return logical.transpose(0, 1, 3, 2, 4, 5).reshape(E, NB * 128, K)[:, :N]
 
