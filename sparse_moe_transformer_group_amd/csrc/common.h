@@ -74,6 +74,16 @@ __device__ __forceinline__ float swiglu(float g, float u) {
 
 __device__ __forceinline__ int wave_lane() { return threadIdx.x & 63; }
 
+// The lane index, computed where it is used.  The asm is volatile, so the
+// compiler can neither hoist it nor merge it with an earlier lane index: a
+// kernel-long copy would be spilled under register pressure, and each
+// reload of it waits for every memory access in flight, stores included.
+__device__ __forceinline__ int lane_here() {
+  int l;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+  return l;
+}
+
 // ---- direct-to-LDS buffer loads (tiled GEMM, flash attention)
 typedef __attribute__((address_space(3))) void lds_void;
 

@@ -404,7 +404,12 @@ __global__ __launch_bounds__(256, OCC) void grouped_tiled_kernel(GroupedArgs a) 
       read_ops(ring, 0, af0, ar0, bf0);
       to_bf16(af0, ar0);
       for (int kt = 0; kt < nk; ++kt) {
-        const unsigned char* sb = ring + (kt % STAGES) * Stage;
+        // stage offsets pass through readfirstlane: it keeps the compiler from
+        // strength-reducing kt % STAGES (STAGES = 5) into one loop-carried
+        // address per token block, which spills and then makes every step
+        // wait for all loads in flight (its wait counts do not see the
+        // direct-to-LDS loads); each read is then base + immediate offset
+        const unsigned char* sb = ring + __builtin_amdgcn_readfirstlane((kt % STAGES) * Stage);
         const int ki = min(kt + STAGES - 1, nk - 1);
         const uint32_t st = ring_lds + (ki % STAGES) * Stage;
         const uint32_t so = (uint32_t)ki * (kBK * 2);
@@ -433,7 +438,7 @@ __global__ __launch_bounds__(256, OCC) void grouped_tiled_kernel(GroupedArgs a) 
         // kt are done; after the barrier, the same holds for every wave
         BEAM_STEP_BARRIER((STAGES - 2) * LPS);
         // next step's first operands (after the last step: a stale stage, unused)
-        read_ops(ring + ((kt + 1) % STAGES) * Stage, 0, af0, ar0, bf0);
+        read_ops(ring + __builtin_amdgcn_readfirstlane(((kt + 1) % STAGES) * Stage), 0, af0, ar0, bf0);
 #pragma unroll
         for (int m = 0; m < 2 * NB; ++m) {
           if ((m >> 1) >= 8)
@@ -451,11 +456,35 @@ __global__ __launch_bounds__(256, OCC) void grouped_tiled_kernel(GroupedArgs a) 
       }
 
       // Epilogue: acc[b][j][i] is row 8*(i/4) + 4*g + (i%4) of this wave's
-      // weight block b, token m0 + 32*j + r.
+      // weight block b, token m0 + 32*j + r.  The lane coordinates are
+      // recomputed here (lane_here) and the FP8 row scales are loaded before
+      // the first store: a load issued after stores (a spill reload
+      // included) waits for all of them.
+      const int ln = lane_here();
+      const int er = ln & 31, eg = ln >> 5;
       if constexpr (MAT == 2) {
+      f32x4 sg[4], su[4];  // FP8 row scales of the lane's 4 x 4 gate and up rows
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        sg[q4] = f32x4{1.f, 1.f, 1.f, 1.f};
+        su[q4] = sg[q4];
+        const int f = fw + 8 * q4 + 4 * eg;
+        if constexpr (W8) {
+          if (f < N) {
+            sg[q4] = *reinterpret_cast<const f32x4*>(a.s0 + (int64_t)e * N + f);
+            su[q4] = *reinterpret_cast<const f32x4*>(a.s1 + (int64_t)e * N + f);
+          }
+        }
+      }
+      // one wait for the scales here, on every path, rather than one in
+      // front of each guarded store block
+      if constexpr (W8) {
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) asm volatile("" ::"v"(sg[q4]), "v"(su[q4]));
+      }
 #pragma unroll
       for (int j = 0; j < NB; ++j) {
-        const int tok = m0 + 32 * j + r;
+        const int tok = m0 + 32 * j + er;
         if (tok >= m1) continue;
         const int64_t row = row0 + tok;
 #pragma unroll
@@ -463,17 +492,12 @@ __global__ __launch_bounds__(256, OCC) void grouped_tiled_kernel(GroupedArgs a) 
           // h k-major: feature f of row `row` sits in k-block f/32, chunk
           // (f%32)/8 (swizzled by the row), element f%8; the 4 features
           // f..f+3 share one chunk.
-          const int f = fw + 8 * q4 + 4 * g;
+          const int f = fw + 8 * q4 + 4 * eg;
           if (f >= N) continue;
-          f32x4 sg = f32x4{1.f, 1.f, 1.f, 1.f}, su = sg;
-          if constexpr (W8) {  // FP8 row scales of these 4 gate and up rows
-            sg = *reinterpret_cast<const f32x4*>(a.s0 + (int64_t)e * N + f);
-            su = *reinterpret_cast<const f32x4*>(a.s1 + (int64_t)e * N + f);
-          }
           float h4[4];
 #pragma unroll
           for (int c = 0; c < 4; ++c)
-            h4[c] = swiglu(acc[0][j][4 * q4 + c] * sg[c], acc[1][j][4 * q4 + c] * su[c]);
+            h4[c] = swiglu(acc[0][j][4 * q4 + c] * sg[q4][c], acc[1][j][4 * q4 + c] * su[q4][c]);
           const int64_t off = ((int64_t)(f >> 5) * a.Tk + row) * 32 +
                               ((((f & 31) >> 3) ^ pack_swz((int)row)) << 3) + (f & 7);
           *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + off) =
@@ -490,6 +514,23 @@ __global__ __launch_bounds__(256, OCC) void grouped_tiled_kernel(GroupedArgs a) 
         // spread over all banks.
         constexpr int RS = 1024 + 16;  // staging row stride, bytes
         static_assert(2 * 32 * RS <= STAGES * Stage, "staging fits the ring");
+        f32x4 sd[2][4];  // FP8 row scales of the lane's features (1 past N)
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4) {
+            sd[b][q4] = f32x4{1.f, 1.f, 1.f, 1.f};
+            const int f = fbase + 64 * wave + 32 * b + 8 * q4 + 4 * eg;
+            if constexpr (W8) {
+              if (f < N) sd[b][q4] = *reinterpret_cast<const f32x4*>(a.s0 + (int64_t)e * N + f);
+            }
+          }
+        if constexpr (W8) {  // one wait for the scales, on every path
+#pragma unroll
+          for (int b = 0; b < 2; ++b)
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) asm volatile("" ::"v"(sd[b][q4]));
+        }
 #pragma unroll
         for (int j = 0; j < NB; ++j) {
           unsigned char* stg = ring + (j & 1) * (32 * RS);
@@ -497,24 +538,22 @@ __global__ __launch_bounds__(256, OCC) void grouped_tiled_kernel(GroupedArgs a) 
           for (int b = 0; b < 2; ++b)
 #pragma unroll
             for (int q4 = 0; q4 < 4; ++q4) {
-              const int fl = 64 * wave + 32 * b + 8 * q4 + 4 * g;  // feature within the tile
+              const int fl = 64 * wave + 32 * b + 8 * q4 + 4 * eg;  // feature within the tile
               f32x4 v = f32x4{acc[b][j][4 * q4], acc[b][j][4 * q4 + 1], acc[b][j][4 * q4 + 2],
                               acc[b][j][4 * q4 + 3]};
-              if constexpr (W8) {
-                if (fbase + fl < N) v *= *reinterpret_cast<const f32x4*>(a.s0 + (int64_t)e * N + fbase + fl);
-              }
-              *reinterpret_cast<f32x4*>(stg + r * RS + fl * 4) = v;
+              if constexpr (W8) v *= sd[b][q4];
+              *reinterpret_cast<f32x4*>(stg + er * RS + fl * 4) = v;
             }
           asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
           __builtin_amdgcn_s_barrier();
           asm volatile("" ::: "memory");
-          const int f = fbase + 4 * lane;
+          const int f = fbase + 4 * ln;
 #pragma unroll
           for (int i = 0; i < 8; ++i) {
             const int rr = 8 * wave + i;  // token of the block, wave-uniform
             const int tok = m0 + 32 * j + rr;
             if (tok < m1 && f < N) {
-              const f32x4 v = *reinterpret_cast<const f32x4*>(stg + rr * RS + lane * 16);
+              const f32x4 v = *reinterpret_cast<const f32x4*>(stg + rr * RS + ln * 16);
               const int64_t at = (int64_t)(row0 + tok) * N + f;
               if (a.out_bf16)  // plain GEMM with a bf16 result (one RNE per value)
                 *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + at) =
