@@ -45,12 +45,14 @@ def replay_matches_eager(fn, x_static, inputs):
         del junk
 
 
+@pytest.mark.parametrize("weights", ["bf16", "fp8"])
 @pytest.mark.parametrize("schedule", ["stream", "tiled"])
-def test_graph_moe_block(bm, schedule):
+def test_graph_moe_block(bm, schedule, weights):
     shape = BlockShape(T=256, H=320, I=384)
-    print(f"[case] graph moe block T={shape.T} schedule={schedule}", flush=True)
+    print(f"[case] graph moe block T={shape.T} schedule={schedule} weights={weights}", flush=True)
     inp = MI.make_block_inputs(shape, DEV, case=11)
-    packed = bm.pack_experts(inp.wg, inp.wu, inp.wd)
+    pack = bm.pack_experts_fp8 if weights == "fp8" else bm.pack_experts
+    packed = pack(inp.wg, inp.wu, inp.wd)
     bm.set_schedule(schedule)
     try:
         def fn(x):
@@ -74,12 +76,35 @@ def test_graph_attention(bm, global_layer):
     replay_matches_eager(fn, us[0].clone(), us)
 
 
-def test_graph_dense(bm):
+@pytest.mark.parametrize("fp8", [False, True])
+def test_graph_dense(bm, fp8):
     T, H, I = 200, 256, 512
-    print(f"[case] graph dense T={T}", flush=True)
-    packed = bm.pack_dense(*MI.make_dense_weights(H, I, DEV, case=13), chunks=2)
+    print(f"[case] graph dense T={T} fp8={fp8}", flush=True)
+    packed = bm.pack_dense(*MI.make_dense_weights(H, I, DEV, case=13), chunks=2, fp8=fp8)
 
     def fn(x):
         return bm.dense_mlp(x, *packed)
     xs = [MI.make_x(T, H, case=c).to(DEV) for c in (41, 42, 43)]
+    replay_matches_eager(fn, xs[0].clone(), xs)
+
+
+@pytest.mark.parametrize("weights", ["bf16", "fp8"])
+def test_graph_sublayer_stack(bm, weights):
+    """Two stacked sublayers (norms, block, residual update), in place on the
+    FP32 stream, captured as one graph."""
+    shape = BlockShape(T=192, H=256, I=128)
+    print(f"[case] graph sublayer stack T={shape.T} weights={weights}", flush=True)
+    pack = bm.pack_experts_fp8 if weights == "fp8" else bm.pack_experts
+    layers = []
+    for layer in range(2):
+        wr = MI.make_router(shape.E, shape.H, layer=layer, case=15).to(DEV)
+        layers.append((wr, pack(*MI.make_expert_weights(shape.E, shape.H, shape.I, DEV, layer=layer,
+                                                       case=15))))
+
+    def fn(s):
+        for step, (wr, packed) in zip((2, 3), layers):
+            bm.sublayer(s, step, wr, *packed, shape.groups, shape.topk_groups, shape.k, shape.scale,
+                        keep_io=False)
+        return s
+    xs = [bm.stream_init(MI.make_x(shape.T, shape.H, case=c).to(DEV)) for c in (51, 52, 53)]
     replay_matches_eager(fn, xs[0].clone(), xs)
