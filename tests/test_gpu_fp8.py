@@ -10,6 +10,7 @@ import moe_inputs as MI
 import oracle as O
 from moe_inputs import BlockShape, bf16_bits
 
+from layouts import fp8_chunk_swizzle
 from parity import check_output, check_routing, keep_mask, sync
 
 pytestmark = pytest.mark.gpu
@@ -27,13 +28,11 @@ def bm():
 def unpack_fp8(data, E, N, K):
     """Codes [E, N, K] from the packed FP8 layout (numpy index arithmetic:
     blocks of 128 rows x 32 k in (row block, k-block) order, 8-byte chunk c of
-    block row j stored at c ^ s(j), s(j) = (j2 ^ j4) + 2 j3 from bits 2..4
-    of j)."""
+    block row j stored at c ^ fp8_chunk_swizzle(j))."""
     NB, KB = -(-N // 128), K // 32
     b = np.asarray(data).reshape(E, NB, KB, 128, 4, 8)
     j = np.arange(128)[:, None]
-    s = (((j >> 2) ^ (j >> 4)) & 1) | ((j >> 2) & 2)
-    phys = np.arange(4)[None, :] ^ s                    # logical chunk c sits at phys[j, c]
+    phys = np.arange(4)[None, :] ^ fp8_chunk_swizzle(j)  # logical chunk c sits at phys[j, c]
     logical = b[:, :, :, j, phys, :]                    # e, rb, kb, j, c, 8
     return logical.transpose(0, 1, 3, 2, 4, 5).reshape(E, NB * 128, K)[:, :N]
 
