@@ -11,6 +11,7 @@ import moe_inputs as MI
 import oracle as O
 from moe_inputs import BlockShape, bf16_bits
 
+from layouts import bf16_chunk_swizzle
 from parity import (check_output, check_routing, keep_mask, oracle_route, sync)
 
 pytestmark = pytest.mark.gpu
@@ -122,8 +123,7 @@ def pack_layout_reference(bits):
     pad[:, :N] = bits
     blocks = pad.reshape(E, NB, 128, KB, 4, 8).transpose(0, 1, 3, 2, 4, 5)  # e, rb, kb, j, c, 8
     j = np.arange(128)[:, None]
-    swz = ((j >> 1) ^ (j >> 2)) & 3
-    logical = np.arange(4)[None, :] ^ swz          # physical slot p holds logical chunk p ^ swz
+    logical = np.arange(4)[None, :] ^ bf16_chunk_swizzle(j)  # physical slot p holds logical chunk p ^ swz
     out = blocks[:, :, :, np.arange(128)[:, None], logical, :]
     return out.reshape(-1)
 

@@ -1,4 +1,4 @@
-"""Host checks of the FP8 packed layout's LDS behaviour.
+"""Host checks of the packed layouts' LDS behaviour.
 
 The tiled GEMM copies each k-step of packed FP8 weights into LDS unchanged
 and then reads an MFMA weight operand as 8 bytes per lane: lane l reads row
@@ -10,7 +10,7 @@ tests pin to the library's packing (layouts.fp8_chunk_swizzle)."""
 import numpy as np
 import pytest
 
-from layouts import fp8_chunk_swizzle
+from layouts import bf16_chunk_swizzle, fp8_chunk_swizzle
 
 
 def conflict_ways(addrs, lanes, banks, width=8):
@@ -50,3 +50,13 @@ def test_fp8_swizzle_repeats_every_32_rows():
     j = np.arange(128)
     np.testing.assert_array_equal(fp8_chunk_swizzle(j), fp8_chunk_swizzle(j % 32))
     assert set(np.unique(fp8_chunk_swizzle(j)).tolist()) == {0, 1, 2, 3}
+
+
+@pytest.mark.parametrize("lanes,banks", [(8, 32), (16, 64)])
+def test_bf16_operand_reads_conflict_free(lanes, banks):
+    """bf16 operands are 16-byte reads of 64-byte rows: lane l reads row
+    l % 32, chunk (2s + l // 32) ^ s(row); the token slab of the tiled GEMM
+    uses the same swizzle."""
+    for s in (0, 1):
+        addrs = [64 * (l % 32) + 16 * ((2 * s + l // 32) ^ int(bf16_chunk_swizzle(l % 32))) for l in range(64)]
+        assert conflict_ways(addrs, lanes, banks, width=16) == 1
