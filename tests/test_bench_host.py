@@ -19,3 +19,17 @@ def test_attention_pairs_beam_shapes():
     # 512*513/2 pairs in the first 512 rows and 512 per row after
     assert bench.attention_pairs(8192, None) == 33_558_528
     assert bench.attention_pairs(8192, 512) == 512 * 513 // 2 + (8192 - 512) * 512
+
+
+def test_gateup_roofline_accounting():
+    # decode: 222 touched experts' gate and up weights, x in, h out; HBM-bound
+    r = bench.gateup_roofline("none", 64, 5120, 2560, 8, 222, 2, 1.0)
+    assert r["algorithmic_per_launch"]["bytes"] == 222 * 2 * 2560 * 5120 * 2 + 64 * 5120 * 2 + 512 * 2560 * 2
+    assert r["algorithmic_per_launch"]["flops"] == 64 * 8 * 4 * 5120 * 2560
+    assert r["bound"] == "hbm" and r["unit"] == "GB/s"
+    assert abs(r["achieved"] - r["algorithmic_per_launch"]["bytes"] / 1e-3 / 1e9) < 0.1
+    # prefill: 256 FLOP per byte is below the 312.5 ridge only by the weights;
+    # at T = 16384 the launch is above it and reported against the MFMA peak
+    r = bench.gateup_roofline("none", 16384, 5120, 2560, 8, 256, 2, 2.0)
+    assert r["bound"] == "mfma" and r["unit"] == "TFLOP/s"
+    assert abs(r["achieved"] - 16384 * 8 * 4 * 5120 * 2560 / 2e-3 / 1e12) < 0.1

@@ -5,7 +5,9 @@ the benchmark times (automatic schedule):
   * decode batch T=64, prefill chunk T=8192, skewed-load T=16384 (Zipf logit
     offsets): routing of every token against the oracle (ids as sets, counts
     after margin exclusion, weights), outputs on sampled tokens that the
-    oracle computes one by one (the block is per-token);
+    oracle computes one by one (the block is per-token); on the skewed batch
+    the sample also holds one token of every token tile of the most loaded
+    expert (the blocked tile order of experts with 8 or more token tiles);
   * four stacked sandwich-normed sublayers at T=4096 with independent
     weights, checked per layer with the device's own layer input (teacher
     forcing), since GPU and oracle layer inputs differ by bf16 rounding that
@@ -49,7 +51,33 @@ def beam_weights(bm):
     torch.cuda.empty_cache()
 
 
-def beam_case(bm, beam_weights, name):
+TILE_TOKENS = 320   # token rows per tile of the prefill-size expert GEMMs
+
+
+def hottest_expert_tile_tokens(ids, keep):
+    """One token from every token tile of the most loaded expert.  Its tokens
+    (ascending, as the permutation orders them) are split evenly over
+    ceil(n / 320) tiles; tile j takes positions [j n / mt, (j + 1) n / mt).
+    The sampled position moves inside each tile so that different rows of
+    the tile (and of its 32-token blocks) are checked; excluded tokens are
+    skipped."""
+    counts = np.bincount(ids.reshape(-1), minlength=256)
+    e = int(np.argmax(counts))
+    toks = np.nonzero((ids == e).any(axis=1))[0]
+    n = toks.size
+    mt = -(-n // TILE_TOKENS)
+    out = []
+    for j in range(mt):
+        lo, hi = j * n // mt, (j + 1) * n // mt
+        for d in range(hi - lo):
+            p = lo + (37 * j + d) % (hi - lo)
+            if keep[toks[p]]:
+                out.append(int(toks[p]))
+                break
+    return e, mt, np.array(out, dtype=np.int64)
+
+
+def beam_case(bm, beam_weights, name, hot_tiles=False):
     shape = MI.WORKLOADS[name]
     print(f"[case] {name} T={shape.T}", flush=True)
     wr, wg, wu, wd, packed = beam_weights
@@ -59,14 +87,20 @@ def beam_case(bm, beam_weights, name):
                                  shape.scale, logit_offset=off)
     sync()
     ref_r = oracle_route(x, wr, shape, off)
-    st = check_routing(ids, w, ref_r, shape.E, counts)
+    st = check_routing(ids, w, ref_r, shape, counts)
     keep = keep_mask(ref_r)
     toks = sample_tokens(keep, N_SAMPLE)
+    if hot_tiles:
+        e_hot, mt_hot, hot = hottest_expert_tile_tokens(ids.cpu().numpy(), keep)
+        assert hot.size == mt_hot >= 8
+        st.update(hottest_expert=e_hot, hottest_expert_tiles=mt_hot)
+        toks = np.unique(np.concatenate([toks, hot]))
     ref = oracle_block_rows(x, toks, wr, wg, wu, wd, shape, off)
     assert np.array_equal(np.sort(ref["ids"], 1), np.sort(ref_r["ids"][toks], 1))
     st.update(check_output(y[torch.from_numpy(toks).to(DEV)], ref["y"]))
     st["sampled_tokens"] = toks.tolist()
-    print({k: v for k, v in st.items() if k != "excluded_tokens"}, flush=True)
+    print({k: v for k, v in st.items() if k not in ("excluded_tokens", "sampled_tokens")},
+          flush=True)
     return counts.cpu().numpy()
 
 
@@ -83,7 +117,7 @@ def test_beam_prefill_T8192(bm, beam_weights):
 
 
 def test_beam_skewed_T16384(bm, beam_weights):
-    counts = beam_case(bm, beam_weights, "skewed")
+    counts = beam_case(bm, beam_weights, "skewed", hot_tiles=True)
     # the offsets make the load strongly skewed (Zipf-like)
     assert counts.max() > 20 * counts.mean()
     assert counts.sum() == 16384 * 8
@@ -110,7 +144,7 @@ def test_beam_stack_T4096_four_sublayers(bm, beam_weights):
         ref_in = O.rmsnorm(prev64)
         assert np.all(np.abs(got_in - ref_in) <= np.abs(ref_in) * 2.0 ** -7 + 1e-30)
         ref_r = oracle_route(xin, wr, shape)          # teacher-forced layer input
-        st = check_routing(ids, w, ref_r, shape.E, counts)
+        st = check_routing(ids, w, ref_r, shape, counts)
         toks = sample_tokens(keep_mask(ref_r), 4)
         ref = O.moe_block(bf16_bits(xin)[toks], bf16_bits(wr), expert_fetcher(wg, wu, wd),
                           shape.groups, shape.topk_groups, shape.k, shape.scale)

@@ -104,7 +104,7 @@ def test_block_fp8_small(bm, schedule, T, H, I, k):
     finally:
         bm.set_schedule("auto")
     ref = oracle_fp8_block(bf16_bits(inp.x), inp.wr, inp.wg, inp.wu, inp.wd, shape)
-    st = check_routing(ids, w, ref, shape.E, counts)
+    st = check_routing(ids, w, ref, shape, counts)
     st.update(check_output(y, ref["y"], keep_mask(ref), out_rounding_slack=(k == 1)))
 
 
@@ -148,7 +148,7 @@ def test_beam_fp8_sampled(bm, beam_fp8, name):
                                  shape.scale)
     sync()
     ref_r = oracle_route(x, wr, shape)
-    check_routing(ids, w, ref_r, shape.E, counts)
+    check_routing(ids, w, ref_r, shape, counts)
     toks = sample_tokens(keep_mask(ref_r), 3)
     ref = oracle_fp8_block(bf16_bits(x)[toks], wr, wg, wu, wd, shape, experts=experts)
     st = check_output(y[torch.from_numpy(toks).to(DEV)], ref["y"])
@@ -177,7 +177,7 @@ def test_sublayer_fp8_teacher_forced(bm, schedule):
             blk = O.stack_sublayer(prev64, step, bf16_bits(wr), fp8_experts_oracle(wg, wu, wd),
                                    shape.groups, shape.topk_groups, shape.k, shape.scale,
                                    moe_input_bits=bf16_bits(xin))
-            check_routing(ids, w, blk, shape.E, counts)
+            check_routing(ids, w, blk, shape, counts)
             print(check_output(yb, blk["y"], keep_mask(blk)))
             ref_stream = O.residual_step(prev64, O.rmsnorm(O.bf16_bits_to_f64(bf16_bits(yb))), step)
             np.testing.assert_allclose(stream.cpu().numpy(), ref_stream, rtol=1e-5, atol=1e-5)

@@ -47,7 +47,7 @@ def full_check(bm, shape, case=0, offset=None, out_rounding_slack=False):
         inp.offset = offset.to(DEV)
     y, ids, w, counts = run_block(bm, inp, shape)
     ref = oracle_full(inp, shape)
-    st = check_routing(ids, w, ref, shape.E, counts)
+    st = check_routing(ids, w, ref, shape, counts)
     st.update(check_output(y, ref["y"], keep_mask(ref), out_rounding_slack))
     print(st)
     return inp, ref, (y, ids, w, counts)
@@ -61,7 +61,7 @@ def test_route_tiny(bm):
     ids, w, counts = bm.route(inp.x, inp.wr, TINY.groups, TINY.topk_groups, TINY.k, TINY.scale)
     sync()
     ref = oracle_route(inp.x, inp.wr, TINY)
-    st = check_routing(ids, w, ref, TINY.E, counts)
+    st = check_routing(ids, w, ref, TINY, counts)
     np.testing.assert_allclose(w.sum(1).cpu().numpy(), 2.5, rtol=0, atol=8 * 2.5 * 2 ** -23)
     print(st)
 
@@ -109,7 +109,7 @@ def test_block_padded_rows(bm, schedule):
     finally:
         bm.set_schedule("auto")
     ref = oracle_full(inp, shape)
-    st = check_routing(ids, w, ref, shape.E, counts)
+    st = check_routing(ids, w, ref, shape, counts)
     st.update(check_output(y, ref["y"], keep_mask(ref)))
 
 
@@ -280,7 +280,7 @@ def test_sublayer_tiny_teacher_forced(bm):
         blk = O.stack_sublayer(prev64, step, bf16_bits(wr),
                                (bf16_bits(wg), bf16_bits(wu), bf16_bits(wd)), shape.groups,
                                shape.topk_groups, shape.k, shape.scale, moe_input_bits=bf16_bits(xin))
-        check_routing(ids, w, blk, shape.E, counts)
+        check_routing(ids, w, blk, shape, counts)
         check_output(yb, blk["y"], keep_mask(blk))
         # residual update from the device's own y
         ref_stream = O.residual_step(prev64, O.rmsnorm(O.bf16_bits_to_f64(bf16_bits(yb))), step)
