@@ -24,7 +24,7 @@ from moe_inputs import bf16_bits
 MARGIN = 1e-6
 REL_L2 = 5e-3
 MAX_ABS_RMS = 2e-2
-W_TOL = 4e-6
+W_TOL = 1e-6
 
 
 def keep_mask(ref, margin=MARGIN):
