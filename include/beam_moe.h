@@ -197,6 +197,35 @@ int beam_moe_block_fp8(void* stream, int64_t T, int H, int I, int E, int groups,
                        int32_t* expert_counts, void* workspace, size_t workspace_bytes);
 
 /*
+ * beam_moe_block without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP-graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc).  The workspace is a static
+ * device array of BEAM_MOE_NOALLOC_SCRATCH_BYTES inside the library, one
+ * per GPU, held from the first call on that GPU until the process ends.
+ * Everything else (arguments, layouts, results, bf16 packed weights) is as
+ * in beam_moe_block; the results are bit-identical to its.
+ *   - The call allocates nothing: no hipMalloc / hipFree, no allocating
+ *     library routine.  Its first call on a device looks up the array's
+ *     device address (hipGetSymbolAddress) and caches it.
+ *   - All calls on one GPU share its array, which keeps the last call's
+ *     contents; everything a call needs zeroed it clears itself with a fill
+ *     kernel.  Calls that overlap on one GPU (different streams or threads
+ *     without ordering) race on the array and give undefined results.
+ *   - WORKSPACE_TOO_SMALL when the sizes need more scratch than the array
+ *     holds (beam_moe_workspace_bytes(T, H, I, E, k) > the maximum); it is
+ *     checked before anything is enqueued.  At the Beam shape (H 5120,
+ *     I 2560, E 256, k 8) T up to 259 fits: decode and speculative-verify
+ *     batches; prefill batches take beam_moe_block.
+ */
+#define BEAM_MOE_NOALLOC_SCRATCH_BYTES (64u << 20)
+int beam_moe_block_noalloc(void* stream, int64_t T, int H, int I, int E, int groups,
+                           int topk_groups, int k, float scale, const uint16_t* x,
+                           const uint16_t* w_router, const float* logit_offset,
+                           const uint16_t* w_gate, const uint16_t* w_up, const uint16_t* w_down,
+                           uint16_t* y, int32_t* topk_ids, float* topk_weights,
+                           int32_t* expert_counts);
+
+/*
  * Residual stream helpers  ([RES]: every sublayer is normalised before and
  * after; the embedding is residual step 1; at step >= 2 the stream keeps
  * sqrt((step-1)/step) of itself and adds 1/sqrt(step) of the sublayer output).

@@ -53,6 +53,9 @@ def _load():
         "beam_moe_block": (_c_int, [_c_vp, _c_i64, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
                                     _c_f, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp,
                                     _c_vp, _c_vp, _c_vp, _c_sz]),
+        "beam_moe_block_noalloc": (_c_int, [_c_vp, _c_i64, _c_int, _c_int, _c_int, _c_int, _c_int,
+                                            _c_int, _c_f, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp,
+                                            _c_vp, _c_vp, _c_vp, _c_vp]),
         "beam_moe_forward_fp8": (_c_int, [_c_vp, _c_i64, _c_int, _c_int, _c_int, _c_int, _c_vp,
                                           _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp,
                                           _c_vp, _c_vp, _c_vp, _c_vp, _c_sz]),
@@ -365,6 +368,44 @@ def block(x, w_router, w_gate, w_up, w_down, groups=8, topk_groups=4, k=8, scale
                             ws.numel())
     _check("beam_moe_block", rc)
     return (y, ids, w, counts) if return_routing else y
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20   # BEAM_MOE_NOALLOC_SCRATCH_BYTES of include/beam_moe.h
+
+
+def block_noalloc(x, w_router, w_gate, w_up, w_down, out, groups=8, topk_groups=4, k=8, scale=2.5,
+                  logit_offset=None, topk_ids=None, topk_weights=None, counts=None):
+    """The whole MoE block (as `block`, bf16 packed weights) with the library's
+    static device scratch as workspace (beam_moe_block_noalloc): nothing is
+    allocated, by the library or here, so every output is the caller's
+    (`out` y [T, H] bf16; optional ids int32 [T, k], weights fp32 [T, k],
+    counts int32 [E]).  Calls on one GPU share the scratch: calls that overlap
+    (different streams) race.  Sizes that need more scratch than the library
+    holds raise ValueError.  Returns `out`."""
+    E, I, H = _expert_shapes(w_gate, w_up, w_down, allow_fp8=False)
+    T = x.shape[0]
+    dev = x.device
+    _dev_tensor(x, "x", torch.bfloat16, (T, H))
+    _dev_tensor(w_router, "w_router", torch.bfloat16, (E, H))
+    _dev_tensor(out, "out", torch.bfloat16, (T, H))
+    if logit_offset is not None:
+        _dev_tensor(logit_offset, "logit_offset", torch.float32, (E,))
+    if topk_ids is not None:
+        _dev_tensor(topk_ids, "topk_ids", torch.int32, (T, k))
+    if topk_weights is not None:
+        _dev_tensor(topk_weights, "topk_weights", torch.float32, (T, k))
+    if counts is not None:
+        _dev_tensor(counts, "counts", torch.int32, (E,))
+    rc = lib.beam_moe_block_noalloc(_stream(dev), T, H, I, E, groups, topk_groups, k, float(scale),
+                                    _ptr(x), _ptr(w_router), _ptr(logit_offset), _ptr(w_gate.data),
+                                    _ptr(w_up.data), _ptr(w_down.data), _ptr(out), _ptr(topk_ids),
+                                    _ptr(topk_weights), _ptr(counts))
+    if rc == -4:
+        raise ValueError(f"beam_moe_block_noalloc: T={T} needs "
+                         f"{workspace_bytes(T, H, I, E, k)} bytes of scratch, more than the "
+                         f"library's {NOALLOC_SCRATCH_BYTES}")
+    _check("beam_moe_block_noalloc", rc)
+    return out
 
 
 def stream_init(x):

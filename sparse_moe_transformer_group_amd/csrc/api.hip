@@ -164,6 +164,34 @@ int device_check(int* num_cu) {
   return BEAM_MOE_OK;
 }
 
+// ---------------------------------------------------------------- static scratch
+// Workspace of beam_moe_block_noalloc, for callers that cannot allocate: a
+// device array of BEAM_MOE_NOALLOC_SCRATCH_BYTES that every GPU the library
+// runs on holds until the process ends.  In host code `scratch` names a host
+// stand-in, not device memory: the device address comes from
+// hipGetSymbolAddress, once per device with that device current, and only
+// that address is ever handed to a kernel.
+static __device__ __align__(256) unsigned char scratch[BEAM_MOE_NOALLOC_SCRATCH_BYTES];
+
+std::atomic<void*> g_scratch_ptr[64];
+std::mutex g_scratch_mu;
+
+int scratch_address(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return BEAM_MOE_ERR_HIP;
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+    if (!p) {
+      if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return BEAM_MOE_ERR_HIP;
+      g_scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return BEAM_MOE_OK;
+}
+
 // ---------------------------------------------------------------- schedule knob
 std::atomic<int> g_schedule{0};  // 0 auto, 1 stream, 2 tiled
 
@@ -509,6 +537,31 @@ int beam_moe_block_fp8(void* stream, int64_t T, int H, int I, int E, int groups,
                    reinterpret_cast<const uint16_t*>(w_down), s_gate, s_up, s_down};
   return block_common(stream, T, H, I, E, groups, topk_groups, k, scale, x, w_router, logit_offset,
                       ex, y, topk_ids, topk_weights, expert_counts, workspace, workspace_bytes);
+}
+
+int beam_moe_block_noalloc(void* stream, int64_t T, int H, int I, int E, int groups,
+                           int topk_groups, int k, float scale, const uint16_t* x,
+                           const uint16_t* w_router, const float* logit_offset,
+                           const uint16_t* w_gate, const uint16_t* w_up, const uint16_t* w_down,
+                           uint16_t* y, int32_t* topk_ids, float* topk_weights,
+                           int32_t* expert_counts) {
+  int rc = check_route_dims(T, H, E, groups, topk_groups, k, scale);
+  if (rc) return rc;
+  if ((rc = check_forward_dims(T, H, I, E, k))) return rc;
+  if (T == 0) return BEAM_MOE_OK;
+  if (layout(T, H, I, E, k).total > (size_t)BEAM_MOE_NOALLOC_SCRATCH_BYTES)
+    return BEAM_MOE_ERR_WORKSPACE_TOO_SMALL;
+  rc = check_ptrs({x, w_router, w_gate, w_up, w_down, y},
+                  {logit_offset, topk_ids, topk_weights, expert_counts});
+  if (rc) return rc;
+  int num_cu;
+  if ((rc = device_check(&num_cu))) return rc;
+  void* ws = nullptr;
+  if ((rc = scratch_address(&ws))) return rc;
+  const Experts ex{w_gate, w_up, w_down, nullptr, nullptr, nullptr};
+  return block_common(stream, T, H, I, E, groups, topk_groups, k, scale, x, w_router, logit_offset,
+                      ex, y, topk_ids, topk_weights, expert_counts, ws,
+                      (size_t)BEAM_MOE_NOALLOC_SCRATCH_BYTES);
 }
 
 int beam_moe_stream_init(void* stream, int64_t T, int H, const uint16_t* x, float* stream_out) {

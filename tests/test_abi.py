@@ -224,3 +224,30 @@ def test_dense_rejects_bad_arguments_on_host():
     assert f8(None, 64, 256, 512, 2, P, P, None, P, P, P, P, P, P, ws) == -2      # gate scales missing
     assert f8(None, 64, 256, 512, 3, P, P, P, P, P, P, P, P, P, ws) == -1         # I % chunks
     assert f8(None, 0, 256, 512, 2, P, P, P, P, P, P, P, P, P, ws) == 0
+
+
+def block_noalloc(T=64, H=5120, I=2560, E=256, G=8, KG=4, k=8, scale=2.5, **kw):
+    a = dict(x=P, wr=P, off=None, wg=P, wu=P, wd=P, y=P, ids=None, w=None, counts=None)
+    a.update(kw)
+    return lib.beam_moe_block_noalloc(None, T, H, I, E, G, KG, k, scale, a["x"], a["wr"], a["off"],
+                                      a["wg"], a["wu"], a["wd"], a["y"], a["ids"], a["w"],
+                                      a["counts"])
+
+
+def test_block_noalloc_validation_and_scratch_limit():
+    """Host-side checks of the no-allocation block (nothing reaches a device):
+    dimension, pointer and alignment errors as in beam_moe_block, and sizes
+    beyond the static scratch rejected before any launch."""
+    assert bm.NOALLOC_SCRATCH_BYTES == 64 << 20
+    assert block_noalloc(G=3) == -1
+    assert block_noalloc(k=40) == -1
+    assert block_noalloc(wr=None) == -2
+    assert block_noalloc(y=None) == -2
+    assert block_noalloc(ids=P + 4) == -3
+    assert block_noalloc(T=0) == 0
+    # the largest Beam-shape batch that fits, and the first that does not
+    fits = max(T for T in range(1, 400)
+               if lib.beam_moe_workspace_bytes(T, 5120, 2560, 256, 8) <= bm.NOALLOC_SCRATCH_BYTES)
+    assert fits == 259
+    assert block_noalloc(T=fits + 1) == -4
+    assert block_noalloc(T=8192) == -4
