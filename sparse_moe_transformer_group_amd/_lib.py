@@ -145,9 +145,28 @@ def workspace_bytes(T: int, H: int, I: int, E: int, k: int) -> int:
     return int(n)
 
 
-def get_workspace(device: torch.device, nbytes: int) -> torch.Tensor:
-    """Per-device workspace buffer, grown on demand and reused across calls."""
-    key = (device.type, device.index)
+def get_workspace(device: torch.device, nbytes: int, workspace: Optional[torch.Tensor] = None
+                  ) -> torch.Tensor:
+    """Workspace for one call on `device` and torch's current stream there.
+
+    With `workspace` (a caller-owned uint8 device tensor) that tensor is used
+    as is.  While the stream is being captured into a graph, a fresh buffer
+    is taken from torch's allocator (the graph's private pool, which keeps
+    the memory for the graph's replays) and nothing is cached.  Otherwise
+    one buffer per (device, stream) is kept and reused, so calls on
+    different streams never share one; it grows on demand, and no captured
+    graph ever addresses a cached buffer, so growing frees nothing a graph
+    still uses."""
+    if workspace is not None:
+        _dev_tensor(workspace, "workspace", torch.uint8)
+        if workspace.device != device:
+            raise ValueError(f"workspace is on {workspace.device}, the call on {device}")
+        if workspace.numel() < nbytes:
+            raise ValueError(f"workspace holds {workspace.numel()} bytes, the call needs {nbytes}")
+        return workspace
+    if torch.cuda.is_current_stream_capturing():
+        return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+    key = (device.index, torch.cuda.current_stream(device).cuda_stream)
     with _ws_lock:
         buf = _ws_cache.get(key)
         if buf is None or buf.numel() < nbytes:
@@ -172,7 +191,7 @@ def set_schedule(mode: str):
 
 
 def route(x, w_router, groups=8, topk_groups=4, k=8, scale=2.5, logit_offset=None,
-          return_counts=True):
+          return_counts=True, workspace=None):
     """Router + group-limited top-k.  Returns (ids int32 [T,k], weights fp32 [T,k], counts)."""
     T, H = x.shape
     E = w_router.shape[0]
@@ -185,7 +204,7 @@ def route(x, w_router, groups=8, topk_groups=4, k=8, scale=2.5, logit_offset=Non
     w = torch.empty((T, k), dtype=torch.float32, device=dev)
     counts = torch.empty((E,), dtype=torch.int32, device=dev) if return_counts else None
     nbytes = workspace_bytes(T, H, 64, E, k)
-    ws = get_workspace(dev, nbytes)
+    ws = get_workspace(dev, nbytes, workspace)
     rc = lib.beam_moe_route(_stream(dev), T, H, E, groups, topk_groups, k, float(scale), _ptr(x),
                             _ptr(w_router), _ptr(logit_offset), _ptr(ids), _ptr(w), _ptr(counts),
                             _ptr(ws), ws.numel())
@@ -193,7 +212,7 @@ def route(x, w_router, groups=8, topk_groups=4, k=8, scale=2.5, logit_offset=Non
     return ids, w, counts
 
 
-def permute(topk_ids, E):
+def permute(topk_ids, E, workspace=None):
     """Expert-major order of the assignments: (counts, offsets, sorted_tokens, row_of)."""
     T, k = topk_ids.shape
     dev = topk_ids.device
@@ -202,7 +221,7 @@ def permute(topk_ids, E):
     offsets = torch.empty((E + 1,), dtype=torch.int32, device=dev)
     sorted_tokens = torch.full((max(T * k, 1),), -1, dtype=torch.int32, device=dev)[:T * k]
     row_of = torch.empty((T * k,), dtype=torch.int32, device=dev)
-    ws = get_workspace(dev, workspace_bytes(T, 64, 64, E, k))
+    ws = get_workspace(dev, workspace_bytes(T, 64, 64, E, k), workspace)
     rc = lib.beam_moe_permute(_stream(dev), T, E, k, _ptr(topk_ids), _ptr(counts), _ptr(offsets),
                               _ptr(sorted_tokens), _ptr(row_of), _ptr(ws), ws.numel())
     _check("beam_moe_permute", rc)
@@ -308,7 +327,7 @@ def _expert_shapes(w_gate, w_up, w_down, allow_fp8=True):
     return E, I, H
 
 
-def forward(x, topk_ids, topk_weights, w_gate, w_up, w_down, return_counts=False):
+def forward(x, topk_ids, topk_weights, w_gate, w_up, w_down, return_counts=False, workspace=None):
     """Experts + combine with given routing; expert weights packed (pack_experts).
     Returns y bf16 [T,H] (and counts)."""
     E, I, H = _expert_shapes(w_gate, w_up, w_down)
@@ -319,7 +338,7 @@ def forward(x, topk_ids, topk_weights, w_gate, w_up, w_down, return_counts=False
     _dev_tensor(topk_weights, "topk_weights", torch.float32, (T, k))
     y = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
     counts = torch.empty((E,), dtype=torch.int32, device=dev) if return_counts else None
-    ws = get_workspace(dev, workspace_bytes(T, H, I, E, k))
+    ws = get_workspace(dev, workspace_bytes(T, H, I, E, k), workspace)
     if isinstance(w_gate, PackedFP8):
         rc = lib.beam_moe_forward_fp8(_stream(dev), T, H, I, E, k, _ptr(x), _ptr(topk_ids),
                                       _ptr(topk_weights), _ptr(w_gate.data), _ptr(w_gate.scales),
@@ -336,7 +355,7 @@ def forward(x, topk_ids, topk_weights, w_gate, w_up, w_down, return_counts=False
 
 
 def block(x, w_router, w_gate, w_up, w_down, groups=8, topk_groups=4, k=8, scale=2.5,
-          logit_offset=None, out=None, return_routing=True):
+          logit_offset=None, out=None, return_routing=True, workspace=None):
     """Whole MoE block; expert weights packed (pack_experts).
     Returns (y, ids, weights, counts) or y."""
     E, I, H = _expert_shapes(w_gate, w_up, w_down)
@@ -353,7 +372,7 @@ def block(x, w_router, w_gate, w_up, w_down, groups=8, topk_groups=4, k=8, scale
         ids = torch.empty((T, k), dtype=torch.int32, device=dev)
         w = torch.empty((T, k), dtype=torch.float32, device=dev)
         counts = torch.empty((E,), dtype=torch.int32, device=dev)
-    ws = get_workspace(dev, workspace_bytes(T, H, I, E, k))
+    ws = get_workspace(dev, workspace_bytes(T, H, I, E, k), workspace)
     if isinstance(w_gate, PackedFP8):
         rc = lib.beam_moe_block_fp8(_stream(dev), T, H, I, E, groups, topk_groups, k, float(scale),
                                     _ptr(x), _ptr(w_router), _ptr(logit_offset), _ptr(w_gate.data),
@@ -435,7 +454,7 @@ def residual_update(stream_io, y, step, eps=1e-6):
 
 
 def sublayer(stream_io, step, w_router, w_gate, w_up, w_down, groups=8, topk_groups=4, k=8,
-             scale=2.5, eps=1e-6, keep_io=True):
+             scale=2.5, eps=1e-6, keep_io=True, workspace=None):
     """One sandwich-normed MoE sublayer + residual update, in place on stream_io
     (expert weights from pack_experts or pack_experts_fp8).  Returns
     (moe_input, moe_output, ids, weights, counts) when keep_io."""
@@ -451,7 +470,7 @@ def sublayer(stream_io, step, w_router, w_gate, w_up, w_down, groups=8, topk_gro
         ids = torch.empty((T, k), dtype=torch.int32, device=dev)
         w = torch.empty((T, k), dtype=torch.float32, device=dev)
         counts = torch.empty((E,), dtype=torch.int32, device=dev)
-    ws = get_workspace(dev, workspace_bytes(T, H, I, E, k))
+    ws = get_workspace(dev, workspace_bytes(T, H, I, E, k), workspace)
     if isinstance(w_gate, PackedFP8):
         rc = lib.beam_moe_sublayer_fp8(_stream(dev), T, H, I, E, groups, topk_groups, k, float(scale),
                                        float(eps), int(step), _ptr(stream_io), _ptr(w_router),
@@ -494,7 +513,7 @@ def attention_workspace_bytes(T: int, H: int) -> int:
     return int(n)
 
 
-def attention(u, w_qkvg, w_o, global_layer, window=512, theta=10000.0, out=None):
+def attention(u, w_qkvg, w_o, global_layer, window=512, theta=10000.0, out=None, workspace=None):
     """Attention sublayer of one sequence at positions 0..T-1 (beam_attn_forward).
     u bf16 [T, H]; weights from pack_attention_weights.  Returns y bf16 [T, H]."""
     T, H = u.shape
@@ -507,7 +526,7 @@ def attention(u, w_qkvg, w_o, global_layer, window=512, theta=10000.0, out=None)
         raise ValueError("packed attention weights do not match the hidden size")
     y = out if out is not None else torch.empty((T, H), dtype=torch.bfloat16, device=dev)
     _dev_tensor(y, "out", torch.bfloat16, (T, H))
-    ws = get_workspace(dev, attention_workspace_bytes(T, H))
+    ws = get_workspace(dev, attention_workspace_bytes(T, H), workspace)
     rc = lib.beam_attn_forward(_stream(dev), T, H, int(bool(global_layer)), int(window),
                                float(theta), _ptr(u), _ptr(w_qkvg.data), _ptr(w_o.data), _ptr(y),
                                _ptr(ws), ws.numel())
@@ -543,7 +562,7 @@ def dense_workspace_bytes(T: int, H: int, I: int, chunks: int) -> int:
     return int(n)
 
 
-def dense_mlp(x, w_gate, w_up, w_down, out=None):
+def dense_mlp(x, w_gate, w_up, w_down, out=None, workspace=None):
     """Dense SwiGLU layer on packed weights from pack_dense.  Returns y bf16 [T, H]."""
     T, H = x.shape
     dev = x.device
@@ -557,7 +576,7 @@ def dense_mlp(x, w_gate, w_up, w_down, out=None):
         raise ValueError("packed dense weights do not match each other or the hidden size")
     y = out if out is not None else torch.empty((T, H), dtype=torch.bfloat16, device=dev)
     _dev_tensor(y, "out", torch.bfloat16, (T, H))
-    ws = get_workspace(dev, dense_workspace_bytes(T, H, C * Ic, C))
+    ws = get_workspace(dev, dense_workspace_bytes(T, H, C * Ic, C), workspace)
     if kind is PackedFP8:
         rc = lib.beam_dense_mlp_fp8(_stream(dev), T, H, C * Ic, C, _ptr(x), _ptr(w_gate.data),
                                     _ptr(w_gate.scales), _ptr(w_up.data), _ptr(w_up.scales),
