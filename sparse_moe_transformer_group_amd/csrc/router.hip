@@ -161,25 +161,47 @@ __global__ __launch_bounds__(256) void select_kernel(const float* __restrict__ z
   const int GS = E / G;
 
   // 1. scores: FP32 sum of the K-slice partials in slice order, + offset, sigmoid.
+  // The loads of up to 16 slices are issued together (one 16-byte load per
+  // slice when the lane's 4 experts are contiguous and aligned), so the
+  // latency is paid once per 16 slices; the sum stays in slice order.
+  float z[EPL];
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) z[i] = 0.f;
+  {
+    const float* zp = zpart + (int64_t)t * E + lane * EPL;
+    const int64_t sstride = (int64_t)T * E;
+    const bool vec4 = (EPL == 4) && (E % 4 == 0) && (lane * EPL + 3 < E);
+    for (int s0 = 0; s0 < S; s0 += 16) {
+      float v[16][EPL];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
+        if (s0 + u >= S) continue;
+        const float* p = zp + (s0 + u) * sstride;
+        if (vec4) {
+          const f32x4 q4 = *reinterpret_cast<const f32x4*>(p);
+#pragma unroll
+          for (int i = 0; i < EPL; ++i) v[u][i] = q4[i & 3];
+        } else {
+#pragma unroll
+          for (int i = 0; i < EPL; ++i) v[u][i] = (lane * EPL + i < E) ? p[i] : 0.f;
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
+        if (s0 + u >= S) continue;
+#pragma unroll
+        for (int i = 0; i < EPL; ++i) z[i] = (s0 + u == 0) ? v[u][i] : z[i] + v[u][i];
+      }
+    }
+  }
   float sc[EPL];
 #pragma unroll
   for (int i = 0; i < EPL; ++i) {
     const int e = lane * EPL + i;
-    float z = 0.f;
     if (e < E) {
-      const float* zp = zpart + (int64_t)t * E + e;
-      const int64_t sstride = (int64_t)T * E;
-      // batches of 8 independent loads, added strictly in slice order
-      for (int s0 = 0; s0 < S; s0 += 8) {
-        float v[8];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) v[u] = (s0 + u < S) ? zp[(s0 + u) * sstride] : 0.f;
-#pragma unroll
-        for (int u = 0; u < 8; ++u)
-          if (s0 + u < S) z = (s0 + u == 0) ? v[u] : z + v[u];
-      }
-      if (offset) z += offset[e];
-      sc[i] = 1.0f / (1.0f + expf(-z));
+      float zi = z[i];
+      if (offset) zi += offset[e];
+      sc[i] = 1.0f / (1.0f + expf(-zi));
     } else {
       sc[i] = -INFINITY;
     }
