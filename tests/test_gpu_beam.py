@@ -5,7 +5,8 @@ the benchmark times (automatic schedule):
   * decode batch T=64, prefill chunk T=8192, skewed-load T=16384 (Zipf logit
     offsets): routing of every token against the oracle (ids as sets, counts
     after margin exclusion, weights), outputs on sampled tokens that the
-    oracle computes one by one (the block is per-token); on the skewed batch
+    oracle computes one by one (the block is per-token) -- every token of the
+    decode batch, 32 / 24 / 8 evenly spread ones of the others; on the skewed batch
     the sample also holds one token of every token tile of the most loaded
     expert (the blocked tile order of experts with 8 or more token tiles);
   * four stacked sandwich-normed sublayers at T=4096 with independent
@@ -77,6 +78,11 @@ def hottest_expert_tile_tokens(ids, keep):
     return e, mt, np.array(out, dtype=np.int64)
 
 
+# outputs checked per workload: every token of the decode batch (element by
+# element at the headline shape), evenly spread samples elsewhere
+N_SAMPLE_OF = {"decode": 64, "verify": 32, "prefill": 24, "skewed": N_SAMPLE}
+
+
 def beam_case(bm, beam_weights, name, hot_tiles=False):
     shape = MI.WORKLOADS[name]
     print(f"[case] {name} T={shape.T}", flush=True)
@@ -89,7 +95,7 @@ def beam_case(bm, beam_weights, name, hot_tiles=False):
     ref_r = oracle_route(x, wr, shape, off)
     st = check_routing(ids, w, ref_r, shape, counts)
     keep = keep_mask(ref_r)
-    toks = sample_tokens(keep, N_SAMPLE)
+    toks = sample_tokens(keep, N_SAMPLE_OF[name])
     if hot_tiles:
         e_hot, mt_hot, hot = hottest_expert_tile_tokens(ids.cpu().numpy(), keep)
         assert hot.size == mt_hot >= 8
