@@ -75,3 +75,33 @@ def test_noalloc_matches_block_beam_decode(bm):
         bm.block_noalloc(MI.make_x(260, shape.H).to(DEV), wr, *packed, y)
     del packed
     torch.cuda.empty_cache()
+
+
+def test_noalloc_captured_graph_replays(bm):
+    """The no-allocation block captured in a HIP graph (its callers' use):
+    replays on rewritten inputs, with eager work and synchronisations between
+    them, equal eager beam_moe_block bit for bit."""
+    shape = BlockShape(T=96, H=256, I=128)
+    print("[case] noalloc graph replay", flush=True)
+    inp = MI.make_block_inputs(shape, DEV, case=57)
+    packed = bm.pack_experts(inp.wg, inp.wu, inp.wd)
+    xs = [MI.make_x(shape.T, shape.H, case=70 + i).to(DEV) for i in range(3)]
+    x_static = xs[0].clone()
+    y_static = torch.empty((shape.T, shape.H), dtype=torch.bfloat16, device=DEV)
+    ids_static = torch.empty((shape.T, shape.k), dtype=torch.int32, device=DEV)
+    bm.block_noalloc(x_static, inp.wr, *packed, y_static, topk_ids=ids_static)   # device checks
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        bm.block_noalloc(x_static, inp.wr, *packed, y_static, topk_ids=ids_static)
+    for x in xs:
+        x_static.copy_(x)
+        g.replay()
+        junk = torch.randn(1 << 18, device=DEV).mul_(2.0).sum()   # eager work between replays
+        torch.cuda.synchronize()
+        y_ref, ids_ref, _, _ = bm.block(x, inp.wr, *packed)
+        torch.cuda.synchronize()
+        assert torch.equal(y_static.view(torch.int16), y_ref.view(torch.int16))
+        assert torch.equal(ids_static, ids_ref)
+        del junk
+    del g
