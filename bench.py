@@ -185,6 +185,20 @@ def gateup_roofline(tag, T, H, I, k, a_mean, wbytes, gu_ms):
     return roof
 
 
+def expert_load(counts):
+    """Realised per-expert load of one batch: tokens per expert (max, mean,
+    min over active experts, the five largest) and the Zipf exponent s of a
+    least-squares fit log(load) = c - s log(rank) over the active experts."""
+    import numpy as np
+    c = np.sort(np.asarray(counts, dtype=np.float64))[::-1]
+    act = c[c > 0]
+    rank = np.arange(1, act.size + 1, dtype=np.float64)
+    s_fit = float(-np.polyfit(np.log(rank), np.log(act), 1)[0]) if act.size > 1 else None
+    return {"max": int(c[0]), "mean": round(float(c.mean()), 2), "min_active": int(act[-1]),
+            "max_over_mean": round(float(c[0] / c.mean()), 2), "top5": [int(v) for v in c[:5]],
+            "fitted_zipf_s": round(s_fit, 3) if s_fit is not None else None}
+
+
 def moe_workload(args, bm, name, wr, pk, host_weights, steps, warmup, graph_replay):
     """Time one MoE workload on resident packed weights; returns its record
     (value, stage times, roofline of gate/up, and the CPU oracle baseline
@@ -224,7 +238,9 @@ def moe_workload(args, bm, name, wr, pk, host_weights, steps, warmup, graph_repl
                                        shape.scale, logit_offset=off)
         active = [int((counts > 0).sum().item())]
         routing = (y_r, ids, w)
+        load = expert_load(counts.cpu().numpy())
     else:
+        load = None
         tmp = stream0.clone()
         active = []
         for l in range(layers):
@@ -295,7 +311,8 @@ def moe_workload(args, bm, name, wr, pk, host_weights, steps, warmup, graph_repl
                    "T": T, "H": H, "I": I, "E": E,
                    "groups": shape.groups, "topk_groups": shape.topk_groups, "k": k,
                    "scale": shape.scale, "layers": layers,
-                   "logit_offset": shape.offset, "active_experts": active},
+                   "logit_offset": shape.offset, "active_experts": active,
+                   "expert_load": load},
         "tflops": round(tflops, 1),
         "frac_peak_mfma": round(tflops / PEAK_BF16_TFLOPS, 4),
         "algorithmic_gbs": round(gbs, 1),

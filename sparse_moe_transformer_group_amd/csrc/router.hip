@@ -95,6 +95,106 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const uint16_t* __re
   }
 }
 
+// Prefill-size batches: a workgroup computes 256 experts x 128 tokens of a
+// K-slice.  The 128-token x slab of a k-step (8 KB) is loaded once per
+// workgroup into LDS (double-buffered, one barrier per step) and shared by
+// the 4 waves; each wave loads its own 64 expert rows from global memory as
+// above.  Per k-step a CU then reads 24 KB for 32 MFMAs per wave instead of
+// 8 KB for 16 (4 waves each loading the same token rows), which kept the
+// kernel on the cache bandwidth.  The k-steps of a slice run in the same
+// order, so the logits are bit-identical to the kernel above.
+__device__ __forceinline__ int xs_swz(int row) { return (row >> 2) & 3; }
+
+__global__ __launch_bounds__(256) void router_logits_wide_kernel(const uint16_t* __restrict__ x,
+                                                                 const uint16_t* __restrict__ wr,
+                                                                 float* __restrict__ zpart, int T,
+                                                                 int H, int E, int S) {
+  __shared__ __attribute__((aligned(16))) unsigned char xs[2][128 * 64];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int r = lane & 15, q = lane >> 4;
+  const int t0 = blockIdx.x * 128;
+  const int e0 = (blockIdx.y * 4 + wave) * 64;  // may be >= E: computes, stores nothing
+  const int s = blockIdx.z;
+  const int nk = H / 32;
+  const int kb = (int)((int64_t)s * nk / S), ke = (int)((int64_t)(s + 1) * nk / S);
+
+  const uint16_t* ap[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) ap[i] = wr + (int64_t)min(e0 + 16 * i + r, E - 1) * H + q * 8;
+  // x slab loads: thread tid copies chunks tid and tid + 256 (row c/4, chunk c%4)
+  const uint16_t* xp[2];
+  int xo[2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int c = tid + 256 * u, row = c >> 2, ch = c & 3;
+    xp[u] = x + (int64_t)min(t0 + row, T - 1) * H + ch * 8;
+    xo[u] = row * 64 + ((ch ^ xs_swz(row)) << 4);
+  }
+  int bo[8];  // this lane's operand of token block j: row 16 j + r, chunk q
+#pragma unroll
+  for (int j = 0; j < 8; ++j) bo[j] = (16 * j + r) * 64 + ((q ^ xs_swz(16 * j + r)) << 4);
+
+  f32x4 acc[4][8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  uint4 a_cur[4], a_nxt[4], x_nxt[2];
+  if (kb < ke) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) a_cur[i] = ld16(ap[i] + kb * 32);
+#pragma unroll
+    for (int u = 0; u < 2; ++u) st16(xs[0] + xo[u], ld16(xp[u] + kb * 32));
+  }
+  __syncthreads();
+  for (int kk = kb; kk < ke; ++kk) {
+    const int buf = (kk - kb) & 1;
+    const bool more = kk + 1 < ke;
+    if (more) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) a_nxt[i] = ld16(ap[i] + (kk + 1) * 32);
+#pragma unroll
+      for (int u = 0; u < 2; ++u) x_nxt[u] = ld16(xp[u] + (kk + 1) * 32);
+    }
+    uint4 b[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) b[j] = *reinterpret_cast<const uint4*>(xs[buf] + bo[j]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) acc[i][j] = mfma16(a_cur[i], b[j], acc[i][j]);
+    if (more) {
+      // the other buffer was last read before the previous barrier
+#pragma unroll
+      for (int u = 0; u < 2; ++u) st16(xs[buf ^ 1] + xo[u], x_nxt[u]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) a_cur[i] = a_nxt[i];
+    }
+    __syncthreads();
+  }
+
+  if (e0 >= E) return;  // after the last barrier
+  float* zs = zpart + (int64_t)s * T * E;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int e = e0 + 16 * i + q * 4;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int t = t0 + 16 * j + r;
+      if (t >= T) continue;
+      float* dst = zs + (int64_t)t * E + e;
+      if (e + 3 < E && (E & 3) == 0) {
+        *reinterpret_cast<f32x4*>(dst) = acc[i][j];
+      } else {
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+          if (e + c < E) dst[c] = acc[i][j][c];
+      }
+    }
+  }
+}
+
 int router_splits(int64_t T, int H, int E) {
   const int64_t blocks = ((T + 63) / 64) * ((E + 255) / 256);
   const int nk = H / 32;
@@ -105,8 +205,13 @@ int router_splits(int64_t T, int H, int E) {
 
 hipError_t launch_router_logits(hipStream_t st, const uint16_t* x, const uint16_t* wr, float* zpart,
                                 int T, int H, int E, int S) {
-  dim3 grid((T + 63) / 64, (E + 255) / 256, S);
-  hipLaunchKernelGGL(router_logits_kernel, grid, dim3(256), 0, st, x, wr, zpart, T, H, E, S);
+  if (T >= 1024) {  // prefill sizes: the 128-token tiles with the x slab in LDS
+    dim3 grid((T + 127) / 128, (E + 255) / 256, S);
+    hipLaunchKernelGGL(router_logits_wide_kernel, grid, dim3(256), 0, st, x, wr, zpart, T, H, E, S);
+  } else {
+    dim3 grid((T + 63) / 64, (E + 255) / 256, S);
+    hipLaunchKernelGGL(router_logits_kernel, grid, dim3(256), 0, st, x, wr, zpart, T, H, E, S);
+  }
   return hipGetLastError();
 }
 

@@ -33,3 +33,14 @@ def test_gateup_roofline_accounting():
     r = bench.gateup_roofline("none", 16384, 5120, 2560, 8, 256, 2, 2.0)
     assert r["bound"] == "mfma" and r["unit"] == "TFLOP/s"
     assert abs(r["achieved"] - 16384 * 8 * 4 * 5120 * 2560 / 2e-3 / 1e12) < 0.1
+
+
+def test_expert_load_stats():
+    import numpy as np
+    # an exact power law load(r) = 1000 r^-1.1 is fitted back to s = 1.1
+    loads = 1000.0 * np.arange(1, 65, dtype=np.float64) ** -1.1
+    st = bench.expert_load(np.concatenate([loads, np.zeros(8)]))
+    assert abs(st["fitted_zipf_s"] - 1.1) < 1e-9
+    assert st["max"] == 1000 and st["top5"][0] == 1000
+    st = bench.expert_load([3, 0, 5, 5])
+    assert st["max"] == 5 and st["min_active"] == 3 and st["mean"] == 3.25

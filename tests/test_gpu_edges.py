@@ -72,3 +72,11 @@ def test_block_largest_hidden(bm, schedule):
 def test_block_largest_intermediate(bm, schedule):
     edge_case(bm, BlockShape(T=3, H=64, I=32768, E=4, groups=2, topk_groups=1, k=2),
               schedule, case=64)
+
+
+def test_block_prefill_router_ragged(bm):
+    """The prefill-size router (128-token tiles, T >= 1024) with a ragged last
+    tile (T = 1100) and fewer experts than a workgroup covers (E = 96: three
+    of its four waves have no experts and only take part in the barriers)."""
+    edge_case(bm, BlockShape(T=1100, H=320, I=128, E=96, groups=12, topk_groups=3, k=6),
+              "auto", case=65)
