@@ -151,7 +151,7 @@ def test_beam_stack_T4096_four_sublayers(bm, beam_weights):
         assert np.all(np.abs(got_in - ref_in) <= np.abs(ref_in) * 2.0 ** -7 + 1e-30)
         ref_r = oracle_route(xin, wr, shape)          # teacher-forced layer input
         st = check_routing(ids, w, ref_r, shape, counts)
-        toks = sample_tokens(keep_mask(ref_r), 4)
+        toks = sample_tokens(keep_mask(ref_r), 12)
         ref = O.moe_block(bf16_bits(xin)[toks], bf16_bits(wr), expert_fetcher(wg, wu, wd),
                           shape.groups, shape.topk_groups, shape.k, shape.scale)
         st.update(check_output(yb[torch.from_numpy(toks).to(DEV)], ref["y"]))
