@@ -13,6 +13,12 @@
 
 namespace beam {
 
+// 8-byte store marked nontemporal, for output written once and not re-read
+// by this kernel.
+__device__ __forceinline__ void st8_nt(void* p, uint2 v) {
+  __builtin_nontemporal_store((uint64_t)v.x | ((uint64_t)v.y << 32), reinterpret_cast<uint64_t*>(p));
+}
+
 // y[t, :] = bf16( sum_j w[t,j] * o[row_of[t*k+j], :] ): FP32 fused multiply-adds
 // in slot order j = 0..k-1, one rounding at the end.  Workgroup (c, t) covers
 // 1024 columns of token t; each thread issues the loads of all its slots
@@ -49,8 +55,9 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
       a3 = fmaf(wj[u], v[u][3], a3);
     }
   }
-  const uint2 pk = make_uint2(pack_bf16x2_rne(a0, a1), pack_bf16x2_rne(a2, a3));
-  *reinterpret_cast<uint2*>(y + t * H + c) = pk;
+  // nontemporal store: 5% faster at T = 8192 (the 84 MB of y compete with
+  // the 1.34 GB read of o; plain stores cost 0.053 ms over a store-free run)
+  st8_nt(y + t * H + c, make_uint2(pack_bf16x2_rne(a0, a1), pack_bf16x2_rne(a2, a3)));
 }
 
 hipError_t launch_combine(hipStream_t st, const float* o, const int32_t* row_of, const float* w, int T,
