@@ -356,10 +356,17 @@ int beam_moe_set_schedule(int mode);
  * into stage_ms[0 .. n_stages-1] (n_stages >= beam_moe_stage_count()), the
  * number of timed calls into *n_calls, and releases the events.  One timer
  * per process; not for concurrent use from several threads.
+ * beam_moe_timer_begin_stages(max_calls, stage_mask) records events only for
+ * the stages whose bit (1u << stage) is set, so that a timed loop carries no
+ * more events than it needs; the other stages read 0 at the end.
+ * beam_moe_timer_begin(n) is beam_moe_timer_begin_stages(n, all stages).
+ * INVALID_DIM for max_calls outside [1, 100000], an empty mask, a bit at or
+ * above beam_moe_stage_count(), or a timer already running.
  */
 int beam_moe_stage_count(void);
 const char* beam_moe_stage_name(int stage);
 int beam_moe_timer_begin(int max_calls);
+int beam_moe_timer_begin_stages(int max_calls, unsigned stage_mask);
 int beam_moe_timer_end(double* stage_ms, int n_stages, int* n_calls);
 
 #ifdef __cplusplus

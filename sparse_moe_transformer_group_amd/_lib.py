@@ -85,6 +85,7 @@ def _load():
         "beam_moe_stage_count": (_c_int, []),
         "beam_moe_stage_name": (ctypes.c_char_p, [_c_int]),
         "beam_moe_timer_begin": (_c_int, [_c_int]),
+        "beam_moe_timer_begin_stages": (_c_int, [_c_int, ctypes.c_uint]),
         "beam_moe_timer_end": (_c_int, [ctypes.POINTER(ctypes.c_double), _c_int,
                                         ctypes.POINTER(_c_int)]),
     }
@@ -594,14 +595,25 @@ def stage_names():
 
 
 class StageTimer:
-    """Per-stage hipEvent timing of the next `max_calls` block/forward calls."""
+    """Per-stage hipEvent timing of the next `max_calls` block/forward calls;
+    `stages` (names from stage_names()) limits the events to those stages,
+    and the result then holds only them."""
 
-    def __init__(self, max_calls: int):
+    def __init__(self, max_calls: int, stages=None):
         self.max_calls = max_calls
+        self.stages = None if stages is None else list(stages)
         self.result = None
 
     def __enter__(self):
-        _check("beam_moe_timer_begin", lib.beam_moe_timer_begin(self.max_calls))
+        if self.stages is None:
+            _check("beam_moe_timer_begin", lib.beam_moe_timer_begin(self.max_calls))
+        else:
+            names = stage_names()
+            unknown = [n for n in self.stages if n not in names]
+            if unknown or not self.stages:
+                raise ValueError(f"unknown or no stages {unknown}; known: {names}")
+            mask = sum(1 << names.index(n) for n in set(self.stages))
+            _check("beam_moe_timer_begin_stages", lib.beam_moe_timer_begin_stages(self.max_calls, mask))
         return self
 
     def __exit__(self, *exc):
@@ -613,5 +625,6 @@ class StageTimer:
             _check("beam_moe_timer_end", rc)
         names = stage_names()
         self.calls = calls.value
-        self.result = {names[i]: arr[i] for i in range(n)}
+        self.result = {names[i]: arr[i] for i in range(n)
+                       if self.stages is None or names[i] in self.stages}
         return False

@@ -223,6 +223,7 @@ const char* kStageNames[NST] = {"router_logits", "select", "permute", "gateup", 
 struct Timer {
   std::mutex mu;
   bool on = false;
+  unsigned mask = 0;           // stages that record events
   int max_calls = 0, n_calls = 0;
   std::vector<hipEvent_t> ev;  // [call][stage][2]
   std::vector<char> used;      // [call][stage]
@@ -238,6 +239,8 @@ struct StageScope {
   int slot, stage;
   hipStream_t st;
   StageScope(int slot_, int stage_, hipStream_t st_) : slot(slot_), stage(stage_), st(st_) {
+    // mask is set before `on`, under the lock that timer_claim takes
+    if (slot >= 0 && !((g_timer.mask >> stage) & 1u)) slot = -1;
     if (slot >= 0) {
       (void)hipEventRecord(g_timer.ev[(size_t)(slot * NST + stage) * 2], st);
       g_timer.used[(size_t)slot * NST + stage] = 1;
@@ -796,8 +799,11 @@ const char* beam_moe_stage_name(int stage) {
   return (stage >= 0 && stage < NST) ? kStageNames[stage] : "";
 }
 
-int beam_moe_timer_begin(int max_calls) {
+int beam_moe_timer_begin(int max_calls) { return beam_moe_timer_begin_stages(max_calls, (1u << NST) - 1u); }
+
+int beam_moe_timer_begin_stages(int max_calls, unsigned stage_mask) {
   if (max_calls < 1 || max_calls > 100000) return BEAM_MOE_ERR_INVALID_DIM;
+  if (stage_mask == 0u || (stage_mask >> NST) != 0u) return BEAM_MOE_ERR_INVALID_DIM;
   std::lock_guard<std::mutex> lk(g_timer.mu);
   if (g_timer.on) return BEAM_MOE_ERR_INVALID_DIM;
   g_timer.ev.assign((size_t)max_calls * NST * 2, nullptr);
@@ -806,6 +812,7 @@ int beam_moe_timer_begin(int max_calls) {
     if (hipEventCreate(&e) != hipSuccess) return BEAM_MOE_ERR_HIP;
   g_timer.max_calls = max_calls;
   g_timer.n_calls = 0;
+  g_timer.mask = stage_mask;
   g_timer.on = true;
   return BEAM_MOE_OK;
 }

@@ -158,6 +158,9 @@ def test_timer_api_without_device():
         b"attn_proj", b"attn_prep", b"attn_flash", b"attn_out"]
     assert lib.beam_moe_stage_name(99) == b""
     assert lib.beam_moe_timer_begin(0) == -1
+    assert lib.beam_moe_timer_begin_stages(0, 1) == -1
+    assert lib.beam_moe_timer_begin_stages(4, 0) == -1                # no stage
+    assert lib.beam_moe_timer_begin_stages(4, 1 << 10) == -1          # no such stage
     n = ctypes.c_int(0)
     arr = (ctypes.c_double * 10)()
     assert lib.beam_moe_timer_end(arr, 10, ctypes.byref(n)) == -1   # not started
