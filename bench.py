@@ -467,19 +467,11 @@ def run_attention(args):
             step()
     torch.cuda.synchronize()
 
-    marks = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
-    with bm.StageTimer(steps) as timer:
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        marks[0].record()
-        for i in range(steps):
-            step()
-            marks[i + 1].record()
-        torch.cuda.synchronize()
-        elapsed = time.perf_counter() - t0
-    step_ms = sorted(marks[i].elapsed_time(marks[i + 1]) for i in range(steps))
-    ms_step = elapsed * 1e3 / steps
-    stage_ms = {n: v / max(timer.calls, 1) for n, v in timer.result.items() if n.startswith("attn_")}
+    # per-stage breakdown (events around every stage) before the timed region,
+    # which then carries the events of the dominant stage only
+    n_breakdown = min(steps, 10)
+    _, _, stage_all = timed_steps(bm, step, n_breakdown, 1)
+    stage_ms = {n: v for n, v in stage_all.items() if n.startswith("attn_")}
 
     pairs = attention_pairs(T, None if glob else ATTN_WINDOW)
     proj_rows = (2 * ATTN_Q + 2 * ATTN_KV) * ATTN_D
@@ -493,17 +485,19 @@ def run_attention(args):
               "attn_out": 2 * T * ATTN_Q * ATTN_D + 2 * ATTN_Q * ATTN_D * H + 2 * T * H}
     total_flops = sum(flops.values())
     dom = max(flops, key=lambda n: stage_ms[n])
+    elapsed, step_ms, stage_timed = timed_steps(bm, step, steps, 1, stages=(dom,))
+    ms_step = elapsed * 1e3 / steps
     kern = {"attn_proj": ("grouped_tiled_kernel<0,...> (q, k, v, gate projection)", "tiled"),
             "attn_flash": ("attn_flash_kernel", os.path.join(CSRC, "attention.hip")),
             "attn_out": ("grouped_tiled_kernel<0,...> (output projection)", "tiled")}[dom]
-    ach = flops[dom] / (stage_ms[dom] * 1e-3) / 1e12
+    ach = flops[dom] / (stage_timed[dom] * 1e-3) / 1e12
     roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
             "frac": round(ach / PEAK_BF16_TFLOPS, 4),
             "traffic": measured_traffic(args.workload, kern[1], dom),
             "clock": measured_clock(args.workload, kern[1], dom),
             "kernel": kern[0], "stage": dom,
             "algorithmic_per_launch": {"bytes": int(nbytes[dom]), "flops": int(flops[dom])},
-            "avg_launch_ms": round(stage_ms[dom], 5)}
+            "avg_launch_ms": round(stage_timed[dom], 5)}
     if args.copy_probe:
         copy_probe(dev)
     per_stage = {n: {"ms": round(stage_ms[n], 5),
@@ -530,6 +524,8 @@ def run_attention(args):
         "tflops": round(total_flops / (ms_step * 1e-3) / 1e12, 1),
         "frac_peak_mfma": round(total_flops / (ms_step * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
         "stages": per_stage,
+        "stages_how": (f"HIP events around every stage of {n_breakdown} steps before the timed "
+                       f"region; inside it only {dom} carries events (roofline)"),
         "roofline": roof,
     }
     if not args.no_cpu_baseline:
@@ -583,19 +579,13 @@ def run_dense(args):
         for _ in range(args.warmup):
             step()
     torch.cuda.synchronize()
-    marks = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
-    with bm.StageTimer(steps) as timer:
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        marks[0].record()
-        for i in range(steps):
-            step()
-            marks[i + 1].record()
-        torch.cuda.synchronize()
-        elapsed = time.perf_counter() - t0
-    step_ms = sorted(marks[i].elapsed_time(marks[i + 1]) for i in range(steps))
+    # the timed region carries gate/up's events only; the breakdown comes
+    # from further steps after it
+    elapsed, step_ms, stage_timed = timed_steps(bm, step, steps, 1, stages=("gateup",))
     ms_step = elapsed * 1e3 / steps
-    stage_ms = {n: v / max(timer.calls, 1) for n, v in timer.result.items()
+    n_breakdown = min(steps, 10)
+    _, _, stage_all = timed_steps(bm, step, n_breakdown, 1)
+    stage_ms = {n: v for n, v in stage_all.items()
                 if n in ("select", "permute", "gateup", "down", "combine")}
     if args.copy_probe:
         copy_probe(dev)
@@ -603,7 +593,7 @@ def run_dense(args):
     wb = 1 if fp8 else 2                                   # bytes per weight
     sb = (lambda rows: 4 * rows) if fp8 else (lambda rows: 0)  # FP8 row scales
     wbytes = 3 * H * I * wb + sb(2 * I + chunks * H)
-    gu_ms = stage_ms["gateup"]
+    gu_ms = stage_timed["gateup"]
     gu_flops, gu_bytes = 4 * T * H * I, 2 * H * I * wb + sb(2 * I) + T * H * 2 + T * I * 2
     schedule = "stream" if T < 20 else "tiled"
     if gu_flops / gu_bytes < PEAK_BF16_TFLOPS / PEAK_HBM_GBS * 1e3:
@@ -641,6 +631,8 @@ def run_dense(args):
         "frac_peak_mfma": round(flops / (ms_step * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
         "algorithmic_gbs": round((wbytes + 4 * T * H) / (ms_step * 1e-3) / 1e9, 1),
         "stage_ms": {n: round(v, 5) for n, v in stage_ms.items()},
+        "stage_ms_how": (f"HIP events around every stage of {n_breakdown} further steps after the "
+                         "timed region; inside it only gate/up carries events (roofline)"),
         "roofline": roof,
     }
     if not args.no_cpu_baseline:
