@@ -275,11 +275,12 @@ int run_route(hipStream_t st, int64_t T, int H, int E, int groups, int topk_grou
 }
 
 int run_permute(hipStream_t st, int64_t T, int E, int k, const int32_t* ids, int32_t* user_counts,
-                const Layout& L, char* ws, int32_t* offsets_out, int32_t* sorted_out, int32_t* rowof_out) {
+                const Layout& L, char* ws, int32_t* offsets_out, int32_t* sorted_out, int32_t* rowof_out,
+                int32_t* clear16 = nullptr) {
   const int64_t Tk = T * k;
   BEAM_TRY(launch_permute(st, ids, Tk, k, E, reinterpret_cast<int32_t*>(ws + L.hist),
                           reinterpret_cast<int32_t*>(ws + L.base), reinterpret_cast<int32_t*>(ws + L.counts),
-                          offsets_out, sorted_out, rowof_out, user_counts));
+                          offsets_out, sorted_out, rowof_out, user_counts, clear16));
   return BEAM_MOE_OK;
 }
 
@@ -304,16 +305,18 @@ int run_forward(hipStream_t st, int64_t T, int H, int I, int E, int k, const uin
   int32_t* rowof = reinterpret_cast<int32_t*>(ws + L.rowof);
   uint16_t* h = reinterpret_cast<uint16_t*>(ws + L.h);
   float* o = reinterpret_cast<float*>(ws + L.o);
-  {
-    StageScope sc(slot, ST_PERMUTE, st);
-    int rc = run_permute(st, T, E, k, ids, user_counts, L, ws, offsets, sorted, rowof);
-    if (rc) return rc;
-  }
   const bool stream = use_stream(T, H, I, k, E);
   int32_t* tctr = reinterpret_cast<int32_t*>(ws + L.tctr);
   {
+    // the tiled GEMMs' tile-claim counters start at 0: cleared by the
+    // permutation's scan workgroup (a kernel store, not a memset: graph-safe)
+    StageScope sc(slot, ST_PERMUTE, st);
+    int rc = run_permute(st, T, E, k, ids, user_counts, L, ws, offsets, sorted, rowof,
+                         stream ? nullptr : tctr);
+    if (rc) return rc;
+  }
+  {
     StageScope sc(slot, ST_GATEUP, st);
-    if (!stream) BEAM_TRY(launch_fill_i32(st, tctr, 16, 0));  // a kernel, not a memset: graph-safe
     GroupedArgs a{x, sorted, ex.wg, ex.wu, ex.sg, ex.su, counts, offsets, h, I, H, E, Tk, tctr};
     if (one) a.m_tiles = tiled_token_tiles(T, I, 2, num_cu);
     BEAM_TRY(stream ? launch_gateup_stream(st, a, T, k) : launch_gateup_tiled(st, a, num_cu));

@@ -23,10 +23,12 @@ hipError_t launch_dense_routing(hipStream_t s, int32_t* ids, float* w, int64_t T
 // ---- permutation (permute.hip) ----
 constexpr int kPermChunk = 512;  // assignments per permutation block
 inline int64_t perm_blocks(int64_t Tk) { return (Tk + kPermChunk - 1) / kPermChunk; }
+// clear16: 16 counters the permutation's single-workgroup kernel sets to 0
+// (the expert GEMMs' tile-claim counters), or null.
 hipError_t launch_permute(hipStream_t s, const int32_t* ids, int64_t Tk, int k, int E,
                           int32_t* block_hist, int32_t* block_base, int32_t* counts,
                           int32_t* offsets, int32_t* sorted_tokens, int32_t* row_of,
-                          int32_t* user_counts);
+                          int32_t* user_counts, int32_t* clear16);
 
 // ---- packed expert weights (pack.hip) ----
 // An expert matrix W[N][K] (bf16, K contiguous) is stored as ceil(N/128) row

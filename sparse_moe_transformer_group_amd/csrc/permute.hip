@@ -43,8 +43,10 @@ __global__ __launch_bounds__(1024) void perm_scan_kernel(const int32_t* __restri
                                                          int32_t* __restrict__ block_base,
                                                          int32_t* __restrict__ counts,
                                                          int32_t* __restrict__ offsets,
-                                                         int32_t* __restrict__ user_counts) {
+                                                         int32_t* __restrict__ user_counts,
+                                                         int32_t* __restrict__ clear16) {
   __shared__ int part[1024];
+  if (clear16 && threadIdx.x < 16) clear16[threadIdx.x] = 0;
   __shared__ int scan[kMaxE];
   const int tid = threadIdx.x;
   const int SL = 1024 / E;  // >= 2 since E <= 512
@@ -141,9 +143,11 @@ __global__ __launch_bounds__(256) void perm_single_kernel(const int32_t* __restr
                                                           int32_t* __restrict__ offsets,
                                                           int32_t* __restrict__ sorted_tokens,
                                                           int32_t* __restrict__ row_of,
-                                                          int32_t* __restrict__ user_counts) {
+                                                          int32_t* __restrict__ user_counts,
+                                                          int32_t* __restrict__ clear16) {
   __shared__ uint32_t mask[kMaxE * kMaskWords];
   __shared__ int hist[kMaxE];
+  if (clear16 && threadIdx.x < 16) clear16[threadIdx.x] = 0;
   __shared__ int scan[kMaxE];
   for (int i = threadIdx.x; i < E * kMaskWords; i += 256) mask[i] = 0u;
   for (int e = threadIdx.x; e < E; e += 256) hist[e] = 0;
@@ -200,16 +204,16 @@ __global__ __launch_bounds__(256) void perm_single_kernel(const int32_t* __restr
 hipError_t launch_permute(hipStream_t st, const int32_t* ids, int64_t Tk, int k, int E,
                           int32_t* block_hist, int32_t* block_base, int32_t* counts,
                           int32_t* offsets, int32_t* sorted_tokens, int32_t* row_of,
-                          int32_t* user_counts) {
+                          int32_t* user_counts, int32_t* clear16) {
   const int64_t NB = perm_blocks(Tk);
   if (NB == 1) {
     hipLaunchKernelGGL(perm_single_kernel, dim3(1), dim3(256), 0, st, ids, (int)Tk, k, E, counts,
-                       offsets, sorted_tokens, row_of, user_counts);
+                       offsets, sorted_tokens, row_of, user_counts, clear16);
     return hipGetLastError();
   }
   hipLaunchKernelGGL(perm_hist_kernel, dim3((unsigned)NB), dim3(256), 0, st, ids, Tk, E, block_hist);
   hipLaunchKernelGGL(perm_scan_kernel, dim3(1), dim3(1024), 0, st, block_hist, (int)NB, E, block_base,
-                     counts, offsets, user_counts);
+                     counts, offsets, user_counts, clear16);
   hipLaunchKernelGGL(perm_scatter_kernel, dim3((unsigned)NB), dim3(256), 0, st, ids, Tk, k, E,
                      block_base, sorted_tokens, row_of);
   return hipGetLastError();
