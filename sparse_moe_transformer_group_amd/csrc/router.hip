@@ -17,7 +17,8 @@ namespace beam {
 // bf16 x bf16 products are exact; MFMA accumulates them in FP32.
 // Each wave computes 64 experts x 64 tokens (4 x 4 MFMA blocks), loading its
 // operands straight from global memory (Wr is 2.6 MB at Beam shape and stays
-// in L2); a workgroup's 4 waves cover 256 experts.  Expert rows are the MFMA
+// in L2); a workgroup's waves (4, or 1 for decode-size batches, which then
+// spread over 4x as many CUs) cover 64 experts each.  Expert rows are the MFMA
 // A side, tokens the B side, so each lane ends with 4 consecutive experts of
 // one token and stores them as one 16-byte vector.
 // ---------------------------------------------------------------------------
@@ -28,7 +29,7 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const uint16_t* __re
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int r = lane & 15, q = lane >> 4;
   const int t0 = blockIdx.x * 64;
-  const int e0 = (blockIdx.y * 4 + wave) * 64;
+  const int e0 = (blockIdx.y * (int)(blockDim.x >> 6) + wave) * 64;
   if (e0 >= E) return;  // no barriers below
   const int s = blockIdx.z;
   const int nk = H / 32;
@@ -195,6 +196,10 @@ __global__ __launch_bounds__(256) void router_logits_wide_kernel(const uint16_t*
   }
 }
 
+// Decode-size batches (one 64-token tile) run the logits with one-wave
+// workgroups of 64 experts: the same per-wave work on 4x as many CUs.
+static bool router_small(int64_t T) { return T <= 64; }
+
 int router_splits(int64_t T, int H, int E) {
   const int64_t blocks = ((T + 63) / 64) * ((E + 255) / 256);
   const int nk = H / 32;
@@ -209,8 +214,9 @@ hipError_t launch_router_logits(hipStream_t st, const uint16_t* x, const uint16_
     dim3 grid((T + 127) / 128, (E + 255) / 256, S);
     hipLaunchKernelGGL(router_logits_wide_kernel, grid, dim3(256), 0, st, x, wr, zpart, T, H, E, S);
   } else {
-    dim3 grid((T + 63) / 64, (E + 255) / 256, S);
-    hipLaunchKernelGGL(router_logits_kernel, grid, dim3(256), 0, st, x, wr, zpart, T, H, E, S);
+    const int W = router_small(T) ? 1 : 4;  // waves per workgroup
+    dim3 grid((T + 63) / 64, (E + 64 * W - 1) / (64 * W), S);
+    hipLaunchKernelGGL(router_logits_kernel, grid, dim3(64 * W), 0, st, x, wr, zpart, T, H, E, S);
   }
   return hipGetLastError();
 }
@@ -248,19 +254,20 @@ __device__ __forceinline__ void merge_top2(float& a1, float& a2, float b1, float
 constexpr int kMaxE = 512;
 constexpr int kMaxG = 256;
 
-// EPL = experts held per lane (lane l holds experts l*EPL .. l*EPL+EPL-1).
-template <int EPL>
-__global__ __launch_bounds__(256) void select_kernel(const float* __restrict__ zpart, int S,
+// EPL = experts held per lane (lane l holds experts l*EPL .. l*EPL+EPL-1);
+// W = waves (tokens) per workgroup: 4, or 1 for decode-size batches.
+template <int EPL, int W>
+__global__ __launch_bounds__(64 * W) void select_kernel(const float* __restrict__ zpart, int S,
                                                      const float* __restrict__ offset, int T, int E,
                                                      int G, int KG, int k, float scale,
                                                      int32_t* __restrict__ ids,
                                                      float* __restrict__ wout,
                                                      int32_t* __restrict__ counts) {
-  __shared__ float lds_sc[4][kMaxE];
-  __shared__ float lds_gs[4][kMaxG];
-  __shared__ int lds_kept[4][kMaxG];
+  __shared__ float lds_sc[W][kMaxE];
+  __shared__ float lds_gs[W][kMaxG];
+  __shared__ int lds_kept[W][kMaxG];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int t_raw = blockIdx.x * 4 + wave;
+  const int t_raw = blockIdx.x * W + wave;
   const bool active = t_raw < T;
   const int t = active ? t_raw : T - 1;
   const int GS = E / G;
@@ -429,10 +436,14 @@ hipError_t launch_select(hipStream_t st, const float* zpart, int S, const float*
                          int groups, int topk_groups, int k, float scale, int32_t* ids, float* w,
                          int32_t* counts) {
   const int epl = (E + 63) / 64;
-  dim3 grid((T + 3) / 4), block(256);
-#define BEAM_SELECT(N)                                                                          \
-  hipLaunchKernelGGL(select_kernel<N>, grid, block, 0, st, zpart, S, offset, T, E, groups,      \
-                     topk_groups, k, scale, ids, w, counts)
+  const bool one = T <= 256;  // one token per workgroup: more CUs for a small batch
+#define BEAM_SELECT(N)                                                                            \
+  if (one)                                                                                        \
+    hipLaunchKernelGGL((select_kernel<N, 1>), dim3(T), dim3(64), 0, st, zpart, S, offset, T, E,   \
+                       groups, topk_groups, k, scale, ids, w, counts);                            \
+  else                                                                                            \
+    hipLaunchKernelGGL((select_kernel<N, 4>), dim3((T + 3) / 4), dim3(256), 0, st, zpart, S,      \
+                       offset, T, E, groups, topk_groups, k, scale, ids, w, counts)
   if (epl <= 1) BEAM_SELECT(1);
   else if (epl <= 2) BEAM_SELECT(2);
   else if (epl <= 4) BEAM_SELECT(4);
