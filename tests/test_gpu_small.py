@@ -75,7 +75,9 @@ def test_block_tiny(bm, schedule):
         bm.set_schedule("auto")
 
 
-@pytest.mark.parametrize("T", [1, 7, 1000])
+# 65: two 64-token router tiles, the second holding one token (4-wave router
+# workgroups); 257: 4-token selection workgroups, the last with one token
+@pytest.mark.parametrize("T", [1, 7, 65, 257, 1000])
 @pytest.mark.parametrize("schedule", ["stream", "tiled"])
 def test_block_ragged_T(bm, T, schedule):
     bm.set_schedule(schedule)
