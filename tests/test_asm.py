@@ -17,7 +17,14 @@ load the compiler waits on with a full count, so one inside a k-loop would
 stall every step behind the direct-to-LDS prefetches in flight.  The check
 finds each innermost loop (a backward branch with no other loop inside) that
 issues MFMAs, in every kernel of the GEMM and attention sources, and asserts
-that no scratch access lies inside one."""
+that no scratch access lies inside one.
+
+Occupancy of the streaming GEMM.  At decode and verify sizes the streaming
+kernel keeps one 8 KB step of weight loads in flight per wave and relies on
+two waves per SIMD (8 per CU, 64 KB in flight: the per-CU optimum of the
+vector-load path; 32 KB streams 10-13% slower).  Its instantiations for one or
+two 16-token tiles must therefore fit 256 registers (arch + accumulation)
+per lane, read from the code object metadata (`.vgpr_count`)."""
 import concurrent.futures as cf
 import os
 import re
@@ -147,3 +154,36 @@ def test_loop_checker_flags_a_spill_in_a_loop():
     assert scratch_in_mfma_loops(outer)[2] == [4]
     assert functions(["_ZN1k1fEv:", "v_nop", ".Lfunc_end0:", "_ZN1k1gEv:", "s_endpgm", ".Lfunc_end1:"]) == \
         {"_ZN1k1fEv": ["v_nop"], "_ZN1k1gEv": ["s_endpgm"]}
+
+
+def register_counts(lines):
+    """Kernel name -> .vgpr_count (arch + accumulation registers) from the
+    code object metadata; entries there start with '- .'."""
+    out, entry = {}, {}
+    for ln in lines:
+        if ln.startswith("- ."):
+            entry = {}
+        m = re.fullmatch(r"-?\s*\.(name|vgpr_count):\s+(\S+)", ln)
+        if m:
+            entry[m.group(1)] = m.group(2)
+            if "name" in entry and "vgpr_count" in entry:
+                out[entry["name"]] = int(entry["vgpr_count"])
+    return out
+
+
+def test_stream_kernels_keep_two_waves_per_simd(asm):
+    regs = register_counts(asm["gemm_stream.hip"])
+    stream = {n: v for n, v in regs.items() if "grouped_stream_kernel" in n}
+    assert len(stream) >= 12, sorted(regs)
+    # template arguments <MAT, RB, MT, W8>: MT is the third
+    small = {n: v for n, v in stream.items()
+             if re.search(r"grouped_stream_kernelILi\d+ELi\d+ELi([12])E", n)}
+    assert len(small) >= 8, sorted(stream)
+    too_big = {n: v for n, v in small.items() if v > 256}
+    assert not too_big, f"fewer than two waves per SIMD: {too_big}"
+
+
+def test_register_count_parser():
+    meta = ["- .agpr_count:     8", ".name:           _ZN4beam1kILi1EEEv", ".vgpr_count:     196",
+            "- .agpr_count:     0", ".vgpr_count:     40", ".name:           _ZN4beam1kILi2EEEv"]
+    assert register_counts(meta) == {"_ZN4beam1kILi1EEEv": 196, "_ZN4beam1kILi2EEEv": 40}
