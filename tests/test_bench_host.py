@@ -44,3 +44,16 @@ def test_expert_load_stats():
     assert st["max"] == 1000 and st["top5"][0] == 1000
     st = bench.expert_load([3, 0, 5, 5])
     assert st["max"] == 5 and st["min_active"] == 3 and st["mean"] == 3.25
+
+
+def test_bench_refuses_several_gpus():
+    """One GPU only: `--gpus N` above 1 exits with status 2 and says why, before
+    any device work."""
+    import os
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120, cwd=root)
+    assert r.returncode == 2, (r.returncode, r.stderr[-500:])
+    assert "one GPU only" in r.stderr and r.stdout == ""
