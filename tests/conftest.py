@@ -7,6 +7,12 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
+# A planted oracle mistake (tests/oracle_mutants.py), applied before any test
+# module imports the oracle; set only by test_oracle_mutants.py's subprocesses.
+if os.environ.get("BEAM_ORACLE_MUTANT"):
+    import oracle_mutants
+    oracle_mutants.apply(os.environ["BEAM_ORACLE_MUTANT"])
+
 
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
