@@ -46,8 +46,8 @@ __global__ __launch_bounds__(1024) void perm_scan_kernel(const int32_t* __restri
                                                          int32_t* __restrict__ user_counts,
                                                          int32_t* __restrict__ clear16) {
   __shared__ int part[1024];
-  if (clear16 && threadIdx.x < 16) clear16[threadIdx.x] = 0;
   __shared__ int scan[kMaxE];
+  if (clear16 && threadIdx.x < 16) clear16[threadIdx.x] = 0;  // the GEMMs' tile-claim counters
   const int tid = threadIdx.x;
   const int SL = 1024 / E;  // >= 2 since E <= 512
   const int e = tid % E, sl = tid / E;
@@ -147,8 +147,8 @@ __global__ __launch_bounds__(256) void perm_single_kernel(const int32_t* __restr
                                                           int32_t* __restrict__ clear16) {
   __shared__ uint32_t mask[kMaxE * kMaskWords];
   __shared__ int hist[kMaxE];
-  if (clear16 && threadIdx.x < 16) clear16[threadIdx.x] = 0;
   __shared__ int scan[kMaxE];
+  if (clear16 && threadIdx.x < 16) clear16[threadIdx.x] = 0;  // the GEMMs' tile-claim counters
   for (int i = threadIdx.x; i < E * kMaskWords; i += 256) mask[i] = 0u;
   for (int e = threadIdx.x; e < E; e += 256) hist[e] = 0;
   __syncthreads();
