@@ -258,11 +258,11 @@ constexpr int kMaxG = 256;
 // W = waves (tokens) per workgroup: 4, or 1 for decode-size batches.
 template <int EPL, int W>
 __global__ __launch_bounds__(64 * W) void select_kernel(const float* __restrict__ zpart, int S,
-                                                     const float* __restrict__ offset, int T, int E,
-                                                     int G, int KG, int k, float scale,
-                                                     int32_t* __restrict__ ids,
-                                                     float* __restrict__ wout,
-                                                     int32_t* __restrict__ counts) {
+                                                         const float* __restrict__ offset, int T, int E,
+                                                         int G, int KG, int k, float scale,
+                                                         int32_t* __restrict__ ids,
+                                                         float* __restrict__ wout,
+                                                         int32_t* __restrict__ counts) {
   __shared__ float lds_sc[W][kMaxE];
   __shared__ float lds_gs[W][kMaxG];
   __shared__ int lds_kept[W][kMaxG];
